@@ -1,0 +1,171 @@
+/*
+ * bpt.h -- C ABI of the MI355X (gfx950) Blockwise Parallel Transformer layer.
+ *
+ * One pre-norm transformer layer computed the blockwise way described in
+ * "Blockwise Parallel Transformer for Long Context Large Models" (§3.2 the
+ * two nested loops, §3.4 the online softmax, Algorithm 1 and the memory
+ * analysis): for every query block, key/value blocks stream through an online
+ * softmax (running max and sum, no s x s score matrix), and the block's
+ * attention output goes straight through the output projection, the residual,
+ * the second norm and the position-wise FFN, so neither the s x s scores nor
+ * the s x ffn_dim FFN intermediate is ever materialised. The backward
+ * recomputes what it needs per query block ("recomputation is also done
+ * blockwise", same page, memory analysis) and rebuilds attention scores from
+ * the saved output and per-row log-sum-exp ("Training memory: model states,
+ * activations and checkpointing", §3, what changes the count: FlashAttention
+ * keeps O and one fp32 log-sum-exp per row and head). An optional head-chunk
+ * loop runs a subset of heads at a time ("Untied Ulysses: Memory-Efficient
+ * Context Parallelism via Headwise Chunking", §3.2 and §3.4).
+ *
+ *   h1 = x + Attn(Norm1(x)) W_o + b_o,   y = h1 + FFN(Norm2(h1))
+ *
+ * Conventions
+ *   - Every pointer argument of the compute entry points is a DEVICE pointer
+ *     (gfx950 global memory) owned by the caller; descriptors and weight /
+ *     gradient tables themselves are host structs read during the call.
+ *   - Row-major, contiguous. y = x W, so a weight is [in, out].
+ *   - The library never allocates device memory: the caller passes the saved
+ *     buffer and a workspace whose sizes the *_size functions return.
+ *   - Work is enqueued asynchronously on the caller's HIP stream; the call
+ *     does not synchronise. Inputs are never modified.
+ *   - All validation happens before the first launch; on a non-zero status
+ *     nothing has been written. A launch failure returns BPT_EHIP (message in
+ *     bpt_last_error()).
+ *   - Thread-safe: no mutable global state besides a thread-local message and
+ *     the opt-in kernel-timing totals (mutex-guarded, see bpt_timing_enable).
+ */
+#ifndef BPT_H_
+#define BPT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BPT_ABI_VERSION 1
+
+typedef enum {
+  BPT_OK = 0,
+  BPT_EINVAL = 1,       /* bad shape, block size, pointer or alignment        */
+  BPT_EWORKSPACE = 2,   /* ws_bytes below bpt_layer_workspace_size()          */
+  BPT_EUNSUPPORTED = 3, /* valid but not built (e.g. head_dim outside 32/64/128) */
+  BPT_EHIP = 4          /* a HIP launch failed                               */
+} bpt_status;
+
+/* Storage type of x, y, dx, weights and the saved buffer. BPT_BF16 stores
+ * bfloat16 and accumulates every product, softmax statistic and norm statistic
+ * in fp32; BPT_F32 stores and computes in fp32. */
+typedef enum { BPT_F32 = 0, BPT_BF16 = 1 } bpt_dtype;
+
+/* LayerNorm: (v - mean) / sqrt(biased var + eps) * g + b.
+ * RMSNorm:   v / sqrt(mean(v^2) + eps) * g. */
+typedef enum { BPT_LAYERNORM = 0, BPT_RMSNORM = 1 } bpt_norm;
+
+/* FFN(z) = act(z W_1 + b_1) W_2 + b_2 with act = ReLU or exact-erf GeLU, or
+ * SwiGLU: (silu(z W_1 + b_1) * (z W_3)) W_2 + b_2 (W_1 = gate, W_3 = up). */
+typedef enum { BPT_RELU = 0, BPT_GELU_ERF = 1, BPT_SWIGLU = 2 } bpt_ffn;
+
+typedef struct {
+  int32_t abi_version; /* = BPT_ABI_VERSION */
+  int32_t dtype;       /* bpt_dtype */
+  int32_t norm;        /* bpt_norm */
+  int32_t ffn;         /* bpt_ffn */
+  int32_t causal;      /* 1: key j visible to query i iff j <= i */
+  int32_t use_rope;    /* 1: rotate pairs (2i, 2i+1) of Q and K by p * rope_base^(-2i/d) */
+  int64_t batch;       /* independent sequences */
+  int64_t seq_len;     /* s; multiple of 16 */
+  int64_t hidden;      /* h = n_heads * head_dim; multiple of 64 */
+  int64_t n_heads;     /* query heads H */
+  int64_t n_kv_heads;  /* KV heads; divides H; query head q uses KV head q / (H / n_kv_heads) */
+  int64_t head_dim;    /* d in {32, 64, 128} */
+  int64_t ffn_dim;     /* f; multiple of 64 */
+  int64_t q_block;     /* c_q: rows per BPT query block (the FFN block); divides s, multiple of 8 */
+  int64_t kv_block;    /* c_kv: key/value block of the online softmax; divides s. Results do not
+                          depend on it; the kernel streams K/V through LDS in 64-row tiles. */
+  int64_t head_chunk;  /* U: query heads per stage; divides H and is a multiple of H / n_kv_heads */
+  double rope_base;    /* e.g. 500000.0 */
+  float norm_eps;      /* e.g. 1e-5 */
+  int32_t reserved;
+} bpt_layer_desc;
+
+/* Layer weights, storage dtype. w_qkv is [h, (H + 2 n_kv_heads) d] packed Q | K | V, head k in
+ * columns [k d, (k+1) d) of its part; w_o [H d, h]; w_1 [h, f]; w_2 [f, h]; w_3 [h, f] (SwiGLU
+ * only). Biases and norm shifts may be NULL (treated as zero); n1_b / n2_b must be NULL for
+ * RMSNorm. n1_g and n2_g are required. */
+typedef struct {
+  const void *w_qkv, *b_qkv, *w_o, *b_o, *w_1, *b_1, *w_2, *b_2, *w_3;
+  const void *n1_g, *n1_b, *n2_g, *n2_b;
+} bpt_layer_weights;
+
+/* Parameter gradients, fp32, same shapes as the weights. A NULL entry is not
+ * computed. accumulate = 0 overwrites, 1 adds to the existing contents. */
+typedef struct {
+  float *dw_qkv, *db_qkv, *dw_o, *db_o, *dw_1, *db_1, *dw_2, *db_2, *dw_3;
+  float *dn1_g, *dn1_b, *dn2_g, *dn2_b;
+  int32_t accumulate;
+  int32_t reserved;
+} bpt_layer_grads;
+
+/* Host-only check of a descriptor (no device work). */
+bpt_status bpt_layer_validate(const bpt_layer_desc* desc);
+
+/* Bytes of the forward->backward state: the attention output O [b, s, H d] in the storage
+ * dtype plus one fp32 base-2 log-sum-exp per (batch, head, row). Linear in s. Returns 0 for an
+ * invalid descriptor. */
+size_t bpt_layer_saved_size(const bpt_layer_desc* desc);
+
+/* Workspace bytes for the forward (backward = 0) or the backward (backward = 1). Affine in s
+ * with no s * ffn_dim term (FFN scratch is q_block * ffn_dim). Returns 0 for an invalid
+ * descriptor. */
+size_t bpt_layer_workspace_size(const bpt_layer_desc* desc, int32_t backward);
+
+/* Forward. x, y: [b, s, h]. saved: bpt_layer_saved_size bytes, written here and read by the
+ * backward. ws: workspace (256-byte aligned), contents undefined on return. stream: a
+ * hipStream_t (NULL = the default stream). */
+bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x,
+                             const bpt_layer_weights* w, void* y, void* saved, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Recompute-based backward. x: the forward's input; saved: the forward's saved buffer;
+ * dy: cotangent of y [b, s, h]; dx: [b, s, h] (storage dtype) written; grads: fp32 parameter
+ * gradients (summed over the batch). */
+bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x,
+                              const bpt_layer_weights* w, const void* saved, const void* dy,
+                              void* dx, const bpt_layer_grads* grads, void* ws, size_t ws_bytes,
+                              void* stream);
+
+const char* bpt_status_string(bpt_status status);
+
+/* ---- Kernel timing (instrumentation for benchmarks and profiling) ----
+ * When a class is enabled, every launch of that kernel class is bracketed by
+ * HIP events recorded on the same stream; bpt_timing_read() waits for the
+ * recorded events and returns, per class, the summed event-to-event duration
+ * in milliseconds and the number of launches since the last reset. The state
+ * is process-wide (shared by all threads and devices); calls that overlap
+ * while timing is enabled are attributed to whichever class they launch. */
+typedef enum {
+  BPT_KERNEL_ATTN_FWD = 0, /* blockwise attention forward                      */
+  BPT_KERNEL_ATTN_BWD = 1, /* attention backward (dK, dV, dQ accumulation)     */
+  BPT_KERNEL_GEMM = 2,     /* projections and FFN GEMMs with fused epilogues   */
+  BPT_KERNEL_ROWWISE = 3,  /* norms, reductions, RoPE table, fills, dQ/D passes */
+  BPT_KERNEL_CLASSES = 4
+} bpt_kernel_class;
+
+/* Enable timing for the classes whose bit (1 << class) is set; 0 disables. */
+bpt_status bpt_timing_enable(uint32_t class_mask);
+
+/* total_ms[BPT_KERNEL_CLASSES] and launches[BPT_KERNEL_CLASSES] (host arrays,
+ * either may be NULL); reset = 1 clears the totals. Returns BPT_EHIP if an
+ * event query fails. */
+bpt_status bpt_timing_read(double* total_ms, int64_t* launches, int32_t reset);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* bpt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPT_H_ */

@@ -1,0 +1,275 @@
+"""Python binding of the MI355X Blockwise Parallel Transformer layer library.
+
+The compute runs in ``libbpt.so`` (HIP kernels for gfx950, built in-tree by
+``memory_efficient_long_amd.build``); this module only marshals arguments
+through the C ABI declared in ``include/bpt.h``. The functions carry the C
+names (``bpt_layer_forward`` ...). PyTorch supplies device memory and the
+stream. There is no fallback: if the library is missing, importing the binding
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+__all__ = [
+    "LayerConfig", "BptLayerDesc", "BptLayerWeights", "BptLayerGrads", "BptError",
+    "load_library", "bpt_layer_validate", "bpt_layer_saved_size", "bpt_layer_workspace_size",
+    "bpt_layer_forward", "bpt_layer_backward", "bpt_status_string", "bpt_last_error",
+    "forward", "backward", "WEIGHT_NAMES", "GRAD_NAMES", "bpt_timing_enable", "bpt_timing_read",
+    "KERNEL_CLASSES",
+]
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libbpt.so")
+ABI_VERSION = 1
+
+DTYPES = {"f32": 0, "bf16": 1}
+NORMS = {"layernorm": 0, "rmsnorm": 1}
+FFNS = {"relu": 0, "gelu": 1, "swiglu": 2}
+
+WEIGHT_NAMES = ["w_qkv", "b_qkv", "w_o", "b_o", "w_1", "b_1", "w_2", "b_2", "w_3",
+                "n1_g", "n1_b", "n2_g", "n2_b"]
+GRAD_NAMES = ["dw_qkv", "db_qkv", "dw_o", "db_o", "dw_1", "db_1", "dw_2", "db_2", "dw_3",
+              "dn1_g", "dn1_b", "dn2_g", "dn2_b"]
+
+
+class BptLayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
+        ("ffn", ctypes.c_int32), ("causal", ctypes.c_int32), ("use_rope", ctypes.c_int32),
+        ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64), ("hidden", ctypes.c_int64),
+        ("n_heads", ctypes.c_int64), ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("ffn_dim", ctypes.c_int64), ("q_block", ctypes.c_int64), ("kv_block", ctypes.c_int64),
+        ("head_chunk", ctypes.c_int64), ("rope_base", ctypes.c_double),
+        ("norm_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
+class BptLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class BptLayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES] + [
+        ("accumulate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class BptError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load_library()
+        msg = lib.bpt_status_string(status).decode()
+        detail = lib.bpt_last_error().decode()
+        super().__init__(f"{where}: {msg} (status {status}){': ' + detail if detail else ''}")
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbpt.so (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m memory_efficient_long_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.bpt_layer_validate.argtypes = [P(BptLayerDesc)]
+    lib.bpt_layer_validate.restype = ctypes.c_int
+    lib.bpt_layer_saved_size.argtypes = [P(BptLayerDesc)]
+    lib.bpt_layer_saved_size.restype = ctypes.c_size_t
+    lib.bpt_layer_workspace_size.argtypes = [P(BptLayerDesc), ctypes.c_int32]
+    lib.bpt_layer_workspace_size.restype = ctypes.c_size_t
+    lib.bpt_layer_forward.argtypes = [P(BptLayerDesc), ctypes.c_void_p, P(BptLayerWeights),
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.bpt_layer_forward.restype = ctypes.c_int
+    lib.bpt_layer_backward.argtypes = [P(BptLayerDesc), ctypes.c_void_p, P(BptLayerWeights),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       P(BptLayerGrads), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    lib.bpt_layer_backward.restype = ctypes.c_int
+    lib.bpt_status_string.argtypes = [ctypes.c_int]
+    lib.bpt_status_string.restype = ctypes.c_char_p
+    lib.bpt_last_error.argtypes = []
+    lib.bpt_last_error.restype = ctypes.c_char_p
+    lib.bpt_timing_enable.argtypes = [ctypes.c_uint32]
+    lib.bpt_timing_enable.restype = ctypes.c_int
+    lib.bpt_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int32]
+    lib.bpt_timing_read.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerConfig:
+    """Shape and options of one layer (mirrors bpt_layer_desc)."""
+    seq_len: int
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn_dim: int
+    dtype: str = "bf16"
+    norm: str = "layernorm"
+    ffn: str = "gelu"
+    causal: bool = True
+    rope_base: Optional[float] = None
+    q_block: int = 1024
+    kv_block: int = 2048
+    head_chunk: Optional[int] = None
+    batch: int = 1
+    norm_eps: float = 1e-5
+
+    @staticmethod
+    def from_shape(sh) -> "LayerConfig":
+        return LayerConfig(seq_len=sh.seq_len, hidden=sh.hidden, n_heads=sh.n_heads,
+                           n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, ffn_dim=sh.ffn_dim,
+                           dtype=sh.dtype, norm=sh.norm, ffn=sh.ffn, causal=sh.causal,
+                           rope_base=sh.rope_base, q_block=sh.q_block, kv_block=sh.kv_block,
+                           head_chunk=sh.head_chunk, batch=sh.batch, norm_eps=sh.norm_eps)
+
+    def desc(self) -> BptLayerDesc:
+        return BptLayerDesc(
+            abi_version=ABI_VERSION, dtype=DTYPES[self.dtype], norm=NORMS[self.norm],
+            ffn=FFNS[self.ffn], causal=int(self.causal), use_rope=int(self.rope_base is not None),
+            batch=self.batch, seq_len=self.seq_len, hidden=self.hidden, n_heads=self.n_heads,
+            n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, ffn_dim=self.ffn_dim,
+            q_block=self.q_block, kv_block=self.kv_block,
+            head_chunk=self.head_chunk if self.head_chunk else self.n_heads,
+            rope_base=float(self.rope_base or 0.0), norm_eps=self.norm_eps, reserved=0)
+
+
+def _desc(d) -> BptLayerDesc:
+    return d.desc() if isinstance(d, LayerConfig) else d
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ----------------------------------------------------------------- C-named wrappers
+def bpt_layer_validate(desc) -> int:
+    return load_library().bpt_layer_validate(ctypes.byref(_desc(desc)))
+
+
+def bpt_layer_saved_size(desc) -> int:
+    return load_library().bpt_layer_saved_size(ctypes.byref(_desc(desc)))
+
+
+def bpt_layer_workspace_size(desc, backward: bool) -> int:
+    return load_library().bpt_layer_workspace_size(ctypes.byref(_desc(desc)), int(backward))
+
+
+def bpt_status_string(status: int) -> str:
+    return load_library().bpt_status_string(status).decode()
+
+
+def bpt_last_error() -> str:
+    return load_library().bpt_last_error().decode()
+
+
+KERNEL_CLASSES = ["attn_fwd", "attn_bwd", "gemm", "rowwise"]
+
+
+def bpt_timing_enable(classes) -> int:
+    """Enable HIP-event timing for the named kernel classes (empty: disable)."""
+    mask = 0
+    for c in classes:
+        mask |= 1 << KERNEL_CLASSES.index(c)
+    return load_library().bpt_timing_enable(mask)
+
+
+def bpt_timing_read(reset: bool = True) -> Dict[str, tuple]:
+    """{class: (total_ms, launches)} since the last reset (waits for the events)."""
+    n = len(KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    st = load_library().bpt_timing_read(ms, cnt, int(reset))
+    if st:
+        raise BptError(st, "bpt_timing_read")
+    return {c: (ms[i], cnt[i]) for i, c in enumerate(KERNEL_CLASSES)}
+
+
+def _weights_struct(weights: Dict[str, "object"]) -> BptLayerWeights:
+    return BptLayerWeights(**{n: _ptr(weights.get(n)) for n in WEIGHT_NAMES})
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def bpt_layer_forward(desc, x, weights, y, saved, workspace, stream=None) -> int:
+    """Raw call: every argument is a device tensor (weights: dict by name)."""
+    d = _desc(desc)
+    w = _weights_struct(weights)
+    return load_library().bpt_layer_forward(
+        ctypes.byref(d), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(saved), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def bpt_layer_backward(desc, x, weights, saved, dy, dx, grads, workspace, accumulate=False,
+                       stream=None) -> int:
+    """Raw call: grads is a dict of fp32 device tensors by GRAD_NAMES (missing = not computed)."""
+    d = _desc(desc)
+    w = _weights_struct(weights)
+    g = BptLayerGrads(**{n: _ptr(grads.get(n)) for n in GRAD_NAMES}, accumulate=int(accumulate),
+                      reserved=0)
+    return load_library().bpt_layer_backward(
+        ctypes.byref(d), _ptr(x), ctypes.byref(w), _ptr(saved), _ptr(dy), _ptr(dx),
+        ctypes.byref(g), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+
+
+# ----------------------------------------------------------------- conveniences
+def _alloc_bytes(n: int, device):
+    import torch
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+def forward(cfg: LayerConfig, x, weights, y=None, saved=None, workspace=None, stream=None):
+    """y, saved = forward(cfg, x, weights): allocates what is not passed."""
+    import torch
+    d = cfg.desc()
+    st = bpt_layer_validate(d)
+    if st:
+        raise BptError(st, "bpt_layer_validate")
+    if y is None:
+        y = torch.empty_like(x)
+    if saved is None:
+        saved = _alloc_bytes(bpt_layer_saved_size(d), x.device)
+    if workspace is None:
+        workspace = _alloc_bytes(bpt_layer_workspace_size(d, False), x.device)
+    st = bpt_layer_forward(d, x, weights, y, saved, workspace, stream)
+    if st:
+        raise BptError(st, "bpt_layer_forward")
+    return y, saved
+
+
+def grad_shapes(cfg: LayerConfig, weights) -> Dict[str, tuple]:
+    return {"d" + n: tuple(weights[n].shape) for n in WEIGHT_NAMES if weights.get(n) is not None}
+
+
+def backward(cfg: LayerConfig, x, weights, saved, dy, dx=None, grads=None, workspace=None,
+             accumulate=False, stream=None):
+    """dx, grads = backward(...): fp32 gradients for every weight present."""
+    import torch
+    d = cfg.desc()
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        grads = {k: torch.empty(s, dtype=torch.float32, device=x.device)
+                 for k, s in grad_shapes(cfg, weights).items()}
+    if workspace is None:
+        workspace = _alloc_bytes(bpt_layer_workspace_size(d, True), x.device)
+    st = bpt_layer_backward(d, x, weights, saved, dy, dx, grads, workspace, accumulate, stream)
+    if st:
+        raise BptError(st, "bpt_layer_backward")
+    return dx, grads

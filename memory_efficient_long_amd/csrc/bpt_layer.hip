@@ -1,0 +1,720 @@
+// Host side of the Blockwise Parallel Transformer layer: descriptor
+// validation, workspace planning and the launch sequence of the forward and
+// the recompute-based backward on the caller's stream.
+//
+// Forward per sequence ("Blockwise Parallel Transformer for Long Context Large
+// Models", §3.2 and Algorithm 1; head chunks from "Untied Ulysses", §3.2):
+//   xn = Norm1(x)
+//   for each head chunk: Q, K, V of the chunk's heads (bias, RoPE) -> blockwise
+//                        attention -> O[:, chunk heads] and the per-row LSE
+//   for each query block i of q_block rows:
+//       h1 = x_i + O_i W_o + b_o            (fp32 block scratch)
+//       z  = Norm2(h1); u = act(z W_1 + b_1)  (q_block x ffn_dim scratch only)
+//       y_i = h1 + u W_2 + b_2
+// Backward per sequence: per query block, recompute h1, z, the FFN
+// pre-activation and u, then the FFN/Norm2/O-projection backward; then per
+// head chunk recompute Q, K, V and run the attention backward, the QKV weight
+// gradient and dxn; finally Norm1's backward plus the residual.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/bpt.h"
+#include "attention.hpp"
+#include "gemm.hpp"
+#include "rowwise.hpp"
+
+using namespace bpt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bpt_status fail(bpt_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+#define BPT_TRY(expr)                                  \
+  do {                                                 \
+    bpt_status _st = (expr);                           \
+    if (_st != BPT_OK) return _st;                     \
+  } while (0)
+
+bpt_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(BPT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return BPT_OK;
+}
+
+// ----------------------------------------------------------------- timing
+// Optional event timing of kernel classes (see bpt_timing_enable).
+struct TimingState {
+  std::mutex mu;
+  uint32_t mask = 0;
+  struct Rec { int cls; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[BPT_KERNEL_CLASSES] = {0, 0, 0, 0};
+  int64_t n[BPT_KERNEL_CLASSES] = {0, 0, 0, 0};
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+struct TimedLaunch {
+  int cls; hipStream_t st; hipEvent_t a = nullptr, b = nullptr;
+  TimedLaunch(int c, hipStream_t s) : cls(c), st(s) {
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!(t.mask & (1u << c))) return;
+    for (hipEvent_t* e : {&a, &b}) {
+      if (!t.pool.empty()) { *e = t.pool.back(); t.pool.pop_back(); }
+      else if (hipEventCreate(e) != hipSuccess) *e = nullptr;
+    }
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~TimedLaunch() {
+    if (!a || !b) return;
+    hipEventRecord(b, st);
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.pending.push_back({cls, a, b});
+  }
+};
+
+constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
+constexpr int kNormWaves = 1024;   // waves of the norm backward (partial rows)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ----------------------------------------------------------------- plan
+struct Plan {
+  int dtype, norm, ffn, causal, rope;
+  int64_t b, s, h, H, Hkv, D, f, cq, ckv, U, G, nkvc, qkv_cols, chunk_cols;
+  double rope_base;
+  float eps;
+  size_t esz;  // storage element size
+};
+
+bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
+  if (!d) return fail(BPT_EINVAL, "desc is NULL");
+  if (d->abi_version != BPT_ABI_VERSION) return fail(BPT_EINVAL, "abi_version mismatch");
+  if (d->dtype != BPT_F32 && d->dtype != BPT_BF16) return fail(BPT_EINVAL, "dtype");
+  if (d->norm != BPT_LAYERNORM && d->norm != BPT_RMSNORM) return fail(BPT_EINVAL, "norm");
+  if (d->ffn != BPT_RELU && d->ffn != BPT_GELU_ERF && d->ffn != BPT_SWIGLU)
+    return fail(BPT_EINVAL, "ffn");
+  if (d->causal != 0 && d->causal != 1) return fail(BPT_EINVAL, "causal must be 0 or 1");
+  if (d->use_rope != 0 && d->use_rope != 1) return fail(BPT_EINVAL, "use_rope must be 0 or 1");
+  if (d->batch < 1 || d->batch > (1 << 20)) return fail(BPT_EINVAL, "batch");
+  if (d->seq_len < 16 || d->seq_len % 16 != 0 || d->seq_len > (1 << 24))
+    return fail(BPT_EINVAL, "seq_len must be a positive multiple of 16 (<= 2^24)");
+  if (d->n_heads < 1 || d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads != 0)
+    return fail(BPT_EINVAL, "n_kv_heads must divide n_heads");
+  if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
+    return fail(BPT_EUNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if (d->dtype == BPT_F32 && d->head_dim > 64)
+    return fail(BPT_EUNSUPPORTED, "fp32 mode supports head_dim 32 or 64");
+  if (d->hidden != d->n_heads * d->head_dim)
+    return fail(BPT_EINVAL, "hidden must equal n_heads * head_dim");
+  if (d->hidden % 64 != 0 || d->hidden > 65536) return fail(BPT_EINVAL, "hidden % 64");
+  if (d->ffn_dim < 64 || d->ffn_dim % 64 != 0 || d->ffn_dim > (1 << 20))
+    return fail(BPT_EINVAL, "ffn_dim must be a positive multiple of 64");
+  if (d->q_block < 8 || d->q_block % 8 != 0 || d->seq_len % d->q_block != 0)
+    return fail(BPT_EINVAL, "q_block must be a multiple of 8 dividing seq_len");
+  if (d->kv_block < 1 || d->seq_len % d->kv_block != 0)
+    return fail(BPT_EINVAL, "kv_block must divide seq_len");
+  const int64_t G = d->n_heads / d->n_kv_heads;
+  if (d->head_chunk < 1 || d->n_heads % d->head_chunk != 0 || d->head_chunk % G != 0)
+    return fail(BPT_EINVAL, "head_chunk must divide n_heads and be a multiple of the GQA group");
+  if (d->use_rope && !(d->rope_base > 1.0 && std::isfinite(d->rope_base)))
+    return fail(BPT_EINVAL, "rope_base");
+  if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(BPT_EINVAL, "norm_eps");
+  const int64_t qkv_cols = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
+  if (d->seq_len * std::max<int64_t>(std::max(d->hidden, qkv_cols), d->ffn_dim) >= (int64_t(1) << 40))
+    return fail(BPT_EUNSUPPORTED, "problem too large");
+  p.dtype = d->dtype; p.norm = d->norm; p.ffn = d->ffn; p.causal = d->causal; p.rope = d->use_rope;
+  p.b = d->batch; p.s = d->seq_len; p.h = d->hidden; p.H = d->n_heads; p.Hkv = d->n_kv_heads;
+  p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
+  p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
+  p.chunk_cols = (p.U + 2 * p.nkvc) * p.D;
+  p.rope_base = d->rope_base; p.eps = d->norm_eps;
+  p.esz = d->dtype == BPT_BF16 ? 2 : 4;
+  return BPT_OK;
+}
+
+// Workspace carve-up: a running offset over 256-byte aligned regions.
+struct Carver {
+  char* base; size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename X> X* take(size_t count) {
+    X* r = base ? (X*)(base + off) : nullptr;
+    off = align_up(off + count * sizeof(X), 256);
+    return r;
+  }
+};
+
+template <typename T>
+struct FwdWs {
+  T *xn, *q, *k, *v, *z, *u, *gate;
+  float* h1;
+  float2* rope;
+};
+
+template <typename T>
+FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
+  FwdWs<T> w{};
+  w.xn = c.take<T>(p.s * p.h);
+  w.rope = p.rope ? c.take<float2>(p.s * (p.D / 2)) : nullptr;
+  w.q = c.take<T>(p.U * p.s * p.D);
+  w.k = c.take<T>(p.nkvc * p.s * p.D);
+  w.v = c.take<T>(p.nkvc * p.s * p.D);
+  w.h1 = c.take<float>(p.cq * p.h);
+  w.z = c.take<T>(p.cq * p.h);
+  w.u = c.take<T>(p.cq * p.f);
+  w.gate = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  return w;
+}
+
+template <typename T>
+struct BwdWs {
+  T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t;
+  float *dvec, *dh, *dxn, *dqacc, *h1, *dz, *part, *npart_g, *npart_b;
+  float2* rope;
+};
+
+template <typename T>
+BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
+  BwdWs<T> w{};
+  const int64_t HD = p.H * p.D;
+  w.xn = c.take<T>(p.s * p.h);
+  w.rope = p.rope ? c.take<float2>(p.s * (p.D / 2)) : nullptr;
+  w.dO = c.take<T>(p.s * HD);
+  w.dvec = c.take<float>(p.H * p.s);
+  w.dh = c.take<float>(p.s * p.h);
+  w.dxn = c.take<float>(p.s * p.h);
+  w.q = c.take<T>(p.U * p.s * p.D);
+  w.k = c.take<T>(p.nkvc * p.s * p.D);
+  w.v = c.take<T>(p.nkvc * p.s * p.D);
+  w.dqacc = c.take<float>(p.s * p.U * p.D);
+  w.dqkv = c.take<T>(p.s * p.chunk_cols);
+  w.h1 = c.take<float>(p.cq * p.h);
+  w.z = c.take<T>(p.cq * p.h);
+  w.a = c.take<T>(p.cq * p.f);
+  w.u = c.take<T>(p.cq * p.f);
+  w.up = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  w.da = c.take<T>(p.cq * p.f);
+  w.dup = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  w.dz = c.take<float>(p.cq * p.h);
+  w.dh_t = c.take<T>(p.cq * p.h);
+  const int64_t maxn = std::max<int64_t>(std::max(p.h, p.f), std::max(p.chunk_cols, HD));
+  w.part = c.take<float>(kColsumParts * maxn);
+  w.npart_g = c.take<float>(kNormWaves * p.h);
+  w.npart_b = c.take<float>(kNormWaves * p.h);
+  return w;
+}
+
+size_t fwd_ws_bytes(const Plan& p) {
+  Carver c(nullptr);
+  if (p.dtype == BPT_BF16) carve_fwd<bf16>(c, p); else carve_fwd<float>(c, p);
+  return c.off;
+}
+size_t bwd_ws_bytes(const Plan& p) {
+  Carver c(nullptr);
+  if (p.dtype == BPT_BF16) carve_bwd<bf16>(c, p); else carve_bwd<float>(c, p);
+  return c.off;
+}
+size_t saved_bytes(const Plan& p) {
+  return align_up((size_t)(p.b * p.s * p.H * p.D) * p.esz, 256) + (size_t)(p.b * p.H * p.s) * 4;
+}
+
+// ----------------------------------------------------------------- launchers
+template <typename T, bool AK, bool BK, class Epi>
+bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
+                int64_t N, int64_t K, const Epi& epi, const char* what) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int BM = 128, BN = 128, BKK = sizeof(T) == 2 ? 64 : 32;
+  // Layout invariants of the tile loaders (16-byte vectors along the
+  // contiguous axis, every vector fully inside or outside the matrix).
+  bool ok = M >= 0 && N >= 0 && K >= 0 && M < (1LL << 31) && N < (1LL << 31) && K < (1LL << 31);
+  ok = ok && (AK ? (K % VEC == 0 && lda >= K) : (M % VEC == 0 && lda >= M));
+  ok = ok && (BK ? (K % VEC == 0 && ldb >= K) : (N % VEC == 0 && ldb >= N));
+  ok = ok && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % VEC == 0) &&
+       (ldb % VEC == 0);
+  if (!ok) return fail(BPT_EUNSUPPORTED, std::string("gemm layout invariant: ") + what);
+  const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (nt == 0) return BPT_OK;
+  TimedLaunch tl(BPT_KERNEL_GEMM, st);
+  hipLaunchKernelGGL((gemm_kernel<T, AK, BK, BM, BN, BKK, Epi>), dim3((unsigned)nt), dim3(256), 0,
+                     st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+  return check_launch(what);
+}
+
+template <typename T, typename Tin, typename Tout>
+bpt_status norm_fwd(hipStream_t st, const Plan& p, const Tin* x, int64_t ldx, const T* g,
+                    const T* bta, Tout* out, int64_t ldo, int64_t rows) {
+  const int nch = (int)((p.h / 8 + 63) / 64);
+  const dim3 grid((unsigned)((rows + 3) / 4)), blk(256);
+  const int kind = p.norm == BPT_LAYERNORM ? NORM_LAYER : NORM_RMS;
+  if (rows == 0) return BPT_OK;
+  TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+#define NF(NC) hipLaunchKernelGGL((norm_fwd_kernel<T, Tin, Tout, NC>), grid, blk, 0, st, x, ldx, g, \
+                                  bta, out, ldo, (int)rows, (int)p.h, kind, p.eps)
+  if (nch <= 1) NF(1); else if (nch <= 2) NF(2); else if (nch <= 4) NF(4);
+  else if (nch <= 8) NF(8); else if (nch <= 16) NF(16); else if (nch <= 32) NF(32);
+  else return fail(BPT_EUNSUPPORTED, "hidden too large for norm kernel");
+#undef NF
+  return check_launch("norm_fwd");
+}
+
+template <typename T, typename Tin, typename Tres>
+bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz, const Tin* xin,
+                    int64_t ldx, const T* g, const Tres* res, int64_t ldr, float* out_f, T* out_t,
+                    int64_t ldo, int64_t rows, float* dg, float* db, float* part_g, float* part_b) {
+  if (rows == 0) return BPT_OK;
+  const int nch = (int)((p.h / 8 + 63) / 64);
+  const int kind = p.norm == BPT_LAYERNORM ? NORM_LAYER : NORM_RMS;
+  const int nblk = (int)std::min<int64_t>(kNormWaves / 4, (rows + 3) / 4);
+  float* pg = dg ? part_g : nullptr;
+  float* pb = db ? part_b : nullptr;
+  const dim3 grid(nblk), blk(256);
+  TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+#define NB(NC) hipLaunchKernelGGL((norm_bwd_kernel<T, Tin, Tres, NC>), grid, blk, 0, st, dz, lddz, xin, \
+                                  ldx, g, res, ldr, out_f, out_t, ldo, pg, pb, (int)rows, (int)p.h,  \
+                                  kind, p.eps)
+  if (nch <= 1) NB(1); else if (nch <= 2) NB(2); else if (nch <= 4) NB(4);
+  else if (nch <= 8) NB(8); else if (nch <= 16) NB(16); else if (nch <= 32) NB(32);
+  else return fail(BPT_EUNSUPPORTED, "hidden too large for norm kernel");
+#undef NB
+  BPT_TRY(check_launch("norm_bwd"));
+  const int P = nblk * 4;
+  const dim3 g2((unsigned)((p.h + 255) / 256));
+  if (dg) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pg, P, (int)p.h, dg, 1);
+  if (db) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pb, P, (int)p.h, db, 1);
+  return check_launch("norm_bwd reduce");
+}
+
+// out[col] += sum over rows of X[:, col]
+template <typename Tin>
+bpt_status colsum(hipStream_t st, const Tin* X, int64_t ldx, int64_t rows, int64_t N, float* part,
+                  float* out) {
+  if (!out || rows == 0 || N == 0) return BPT_OK;
+  const int P = (int)std::min<int64_t>(kColsumParts, rows);
+  TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+  hipLaunchKernelGGL(colsum_partial_kernel<Tin>, dim3((unsigned)((N + 63) / 64), P), dim3(256), 0,
+                     st, X, ldx, (int)rows, (int)N, part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+                     part, P, (int)N, out, 1);
+  return check_launch("colsum");
+}
+
+bpt_status fill(hipStream_t st, float* ptr, int64_t n, float v) {
+  if (!ptr || n == 0) return BPT_OK;
+  TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ptr, n, v);
+  return check_launch("fill");
+}
+
+bpt_status rope_table(hipStream_t st, const Plan& p, float2* tab) {
+  if (!p.rope) return BPT_OK;
+  const int64_t n = p.s * (p.D / 2);
+  TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, tab,
+                     (int)p.s, (int)p.D, p.rope_base);
+  return check_launch("rope_table");
+}
+
+template <typename T>
+bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v, T* o,
+                    float* lse) {
+  AttnFwdArgs<T> a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.ldo = p.H * p.D; a.lse = lse;
+  a.s = (int)p.s; a.nh = (int)p.U; a.group = (int)p.G; a.causal = p.causal;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
+  TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
+  if (p.D == 128) hipLaunchKernelGGL((attn_fwd_kernel<T, 128>), grid, blk, 0, st, a);
+  else if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<T, 32>), grid, blk, 0, st, a);
+  return check_launch("attn_fwd");
+}
+
+template <typename T>
+bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v,
+                    const T* dout, const float* lse, const float* dvec, float* dq, T* dk, T* dv,
+                    const float2* rope) {
+  AttnBwdArgs<T> a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lddo = p.H * p.D; a.lse = lse; a.dvec = dvec;
+  a.dq = dq; a.lddq = p.U * p.D; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
+  a.s = (int)p.s; a.nh = (int)p.U; a.nkv = (int)p.nkvc; a.group = (int)p.G; a.causal = p.causal;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  a.scale = (float)(1.0 / std::sqrt((double)p.D));
+  const dim3 grid((unsigned)(p.nkvc * ((p.s + 127) / 128))), blk(256);
+  TimedLaunch tl(BPT_KERNEL_ATTN_BWD, st);
+  if constexpr (sizeof(T) == 2) {
+    if (p.D == 128) {
+      hipLaunchKernelGGL((attn_bwd_kernel<T, 128>), grid, blk, 0, st, a);
+      return check_launch("attn_bwd");
+    }
+  }
+  if (p.D == 128) return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
+  if (p.D == 64) hipLaunchKernelGGL((attn_bwd_kernel<T, 64>), grid, blk, 0, st, a);
+  else hipLaunchKernelGGL((attn_bwd_kernel<T, 32>), grid, blk, 0, st, a);
+  return check_launch("attn_bwd");
+}
+
+// Q, K, V of head chunk c (query heads [c U, (c+1) U)) into head-major buffers.
+template <typename T>
+bpt_status qkv_chunk(hipStream_t st, const Plan& p, const T* xn, const T* wqkv, const T* bqkv,
+                     int64_t c, T* q, T* k, T* v, const float2* rope) {
+  const int64_t hq0 = c * p.U, hk0 = hq0 / p.G;
+  const int64_t cols[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
+  const int64_t widths[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};
+  T* outs[3] = {q, k, v};
+  for (int part = 0; part < 3; ++part) {
+    EpiQKV<T> e{outs[part], p.s * p.D, (int)p.D, bqkv ? bqkv + cols[part] : nullptr,
+                part < 2 ? rope : nullptr, 0};
+    BPT_TRY((gemm<T, true, false>(st, xn, p.h, wqkv + cols[part], p.qkv_cols, p.s, widths[part],
+                                  p.h, e, "qkv projection")));
+  }
+  return BPT_OK;
+}
+
+// ----------------------------------------------------------------- forward
+template <typename T>
+bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, T* y, void* saved,
+                        void* ws, hipStream_t st) {
+  Carver c(ws);
+  FwdWs<T> w = carve_fwd<T>(c, p);
+  const T* wqkv = (const T*)wt->w_qkv; const T* bqkv = (const T*)wt->b_qkv;
+  const T* wo = (const T*)wt->w_o; const T* bo = (const T*)wt->b_o;
+  const T* w1 = (const T*)wt->w_1; const T* b1 = (const T*)wt->b_1;
+  const T* w2 = (const T*)wt->w_2; const T* b2 = (const T*)wt->b_2;
+  const T* w3 = (const T*)wt->w_3;
+  const T* g1 = (const T*)wt->n1_g; const T* sh1 = (const T*)wt->n1_b;
+  const T* g2 = (const T*)wt->n2_g; const T* sh2 = (const T*)wt->n2_b;
+  const int64_t HD = p.H * p.D;
+  T* O = (T*)saved;
+  float* LSE = (float*)((char*)saved + align_up((size_t)(p.b * p.s * HD) * p.esz, 256));
+  BPT_TRY(rope_table(st, p, w.rope));
+  const int act = p.ffn == BPT_RELU ? ACT_RELU : ACT_GELU;
+
+  for (int64_t bi = 0; bi < p.b; ++bi) {
+    const T* xb = x + bi * p.s * p.h;
+    T* yb = y + bi * p.s * p.h;
+    T* Ob = O + bi * p.s * HD;
+    float* Lb = LSE + bi * p.H * p.s;
+    BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
+    for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
+      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
+      BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s));
+    }
+    for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
+      const T* Oi = Ob + r0 * HD;
+      EpiResid<T, T, float> eo{w.h1, p.h, xb + r0 * p.h, p.h, bo};
+      BPT_TRY((gemm<T, true, false>(st, Oi, HD, wo, p.h, p.cq, p.h, HD, eo, "o projection")));
+      BPT_TRY((norm_fwd<T, float, T>(st, p, w.h1, p.h, g2, sh2, w.z, p.h, p.cq)));
+      if (p.ffn == BPT_SWIGLU) {
+        EpiOut<T, T> eg{w.gate, p.f, b1, 1.f, 0};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate")));
+        EpiSwiUp<T> eu{w.u, nullptr, w.gate, p.f};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up")));
+      } else {
+        EpiAct<T> ea{w.u, nullptr, p.f, b1, act};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1")));
+      }
+      EpiResid<T, float, T> ey{yb + r0 * p.h, p.h, w.h1, p.h, b2};
+      BPT_TRY((gemm<T, true, false>(st, w.u, p.f, w2, p.h, p.cq, p.h, p.f, ey, "ffn fc2")));
+    }
+  }
+  return BPT_OK;
+}
+
+// ----------------------------------------------------------------- backward
+template <typename T>
+bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, const void* saved,
+                         const T* dy, T* dx, const bpt_layer_grads* gr, void* ws, hipStream_t st) {
+  Carver c(ws);
+  BwdWs<T> w = carve_bwd<T>(c, p);
+  const T* wqkv = (const T*)wt->w_qkv; const T* bqkv = (const T*)wt->b_qkv;
+  const T* wo = (const T*)wt->w_o; const T* bo = (const T*)wt->b_o;
+  const T* w1 = (const T*)wt->w_1; const T* b1 = (const T*)wt->b_1;
+  const T* w2 = (const T*)wt->w_2;
+  const T* w3 = (const T*)wt->w_3;
+  const T* g1 = (const T*)wt->n1_g; const T* sh1 = (const T*)wt->n1_b;
+  const T* g2 = (const T*)wt->n2_g; const T* sh2 = (const T*)wt->n2_b;
+  const int64_t HD = p.H * p.D;
+  const T* O = (const T*)saved;
+  const float* LSE =
+      (const float*)((const char*)saved + align_up((size_t)(p.b * p.s * HD) * p.esz, 256));
+  const bool swiglu = p.ffn == BPT_SWIGLU;
+  const int act = p.ffn == BPT_RELU ? ACT_RELU : ACT_GELU;
+
+  // Gradients that are computed, with their sizes; zeroed unless accumulating.
+  float* dwqkv = gr->dw_qkv; float* dbqkv = bqkv ? gr->db_qkv : nullptr;
+  float* dwo = gr->dw_o; float* dbo = bo ? gr->db_o : nullptr;
+  float* dw1 = gr->dw_1; float* db1 = b1 ? gr->db_1 : nullptr;
+  float* dw2 = gr->dw_2; float* db2 = wt->b_2 ? gr->db_2 : nullptr;
+  float* dw3 = swiglu ? gr->dw_3 : nullptr;
+  float* dg1 = gr->dn1_g; float* dsh1 = sh1 ? gr->dn1_b : nullptr;
+  float* dg2 = gr->dn2_g; float* dsh2 = sh2 ? gr->dn2_b : nullptr;
+  if (!gr->accumulate) {
+    BPT_TRY(fill(st, dwqkv, p.h * p.qkv_cols, 0.f)); BPT_TRY(fill(st, dbqkv, p.qkv_cols, 0.f));
+    BPT_TRY(fill(st, dwo, HD * p.h, 0.f)); BPT_TRY(fill(st, dbo, p.h, 0.f));
+    BPT_TRY(fill(st, dw1, p.h * p.f, 0.f)); BPT_TRY(fill(st, db1, p.f, 0.f));
+    BPT_TRY(fill(st, dw2, p.f * p.h, 0.f)); BPT_TRY(fill(st, db2, p.h, 0.f));
+    BPT_TRY(fill(st, dw3, p.h * p.f, 0.f));
+    BPT_TRY(fill(st, dg1, p.h, 0.f)); BPT_TRY(fill(st, dsh1, p.h, 0.f));
+    BPT_TRY(fill(st, dg2, p.h, 0.f)); BPT_TRY(fill(st, dsh2, p.h, 0.f));
+  }
+  BPT_TRY(rope_table(st, p, w.rope));
+
+  for (int64_t bi = 0; bi < p.b; ++bi) {
+    const T* xb = x + bi * p.s * p.h;
+    const T* dyb = dy + bi * p.s * p.h;
+    T* dxb = dx + bi * p.s * p.h;
+    const T* Ob = O + bi * p.s * HD;
+    const float* Lb = LSE + bi * p.H * p.s;
+    BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
+
+    // ---- per query block: FFN, Norm2 and O-projection backward
+    for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
+      const T* Oi = Ob + r0 * HD;
+      const T* dyi = dyb + r0 * p.h;
+      EpiResid<T, T, float> eo{w.h1, p.h, xb + r0 * p.h, p.h, bo};
+      BPT_TRY((gemm<T, true, false>(st, Oi, HD, wo, p.h, p.cq, p.h, HD, eo, "o projection (re)")));
+      BPT_TRY((norm_fwd<T, float, T>(st, p, w.h1, p.h, g2, sh2, w.z, p.h, p.cq)));
+      if (swiglu) {
+        EpiOut<T, T> eg{w.a, p.f, b1, 1.f, 0};   // w.a holds the gate pre-activation
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate (re)")));
+        EpiSwiUp<T> eu{w.u, w.up, w.a, p.f};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up (re)")));
+      } else {
+        EpiAct<T> ea{w.u, w.a, p.f, b1, act};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1 (re)")));
+      }
+      if (dw2) {
+        EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyi, p.h, p.f, p.h, p.cq, e, "dW2")));
+      }
+      BPT_TRY(colsum<T>(st, dyi, p.h, p.cq, p.h, w.part, db2));
+      if (swiglu) {
+        EpiSwiGrad<T> e{w.da, w.dup, w.a, w.up, p.f};
+        BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du (swiglu)")));
+      } else {
+        EpiActGrad<T> e{w.da, w.a, p.f, act};
+        BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du")));
+      }
+      if (dw1) {
+        EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, p.cq, e, "dW1")));
+      }
+      if (dw3) {
+        EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, p.cq, e, "dW3")));
+      }
+      BPT_TRY(colsum<T>(st, w.da, p.f, p.cq, p.f, w.part, db1));
+      {
+        EpiOut<T, float> e{w.dz, p.h, nullptr, 1.f, 0};
+        BPT_TRY((gemm<T, true, true>(st, w.da, p.f, w1, p.f, p.cq, p.h, p.f, e, "dz")));
+        if (swiglu) {
+          EpiOut<T, float> e3{w.dz, p.h, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, true, true>(st, w.dup, p.f, w3, p.f, p.cq, p.h, p.f, e3, "dz (up)")));
+        }
+      }
+      float* dh_rows = w.dh + r0 * p.h;
+      BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, w.h1, p.h, g2, dyi, p.h, dh_rows, w.dh_t,
+                                     p.h, p.cq, dg2, dsh2, w.npart_g, w.npart_b)));
+      if (dwo) {
+        EpiOut<T, float> e{dwo, p.h, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, Oi, HD, w.dh_t, p.h, HD, p.h, p.cq, e, "dWo")));
+      }
+      BPT_TRY(colsum<float>(st, dh_rows, p.h, p.cq, p.h, w.part, dbo));
+      {
+        EpiOut<T, T> e{w.dO + r0 * HD, HD, nullptr, 1.f, 0};
+        BPT_TRY((gemm<T, true, true>(st, w.dh_t, p.h, wo, p.h, p.cq, HD, p.h, e, "dO")));
+      }
+    }
+
+    // ---- attention backward per head chunk
+    {
+    TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+    hipLaunchKernelGGL(attn_dvec_kernel<T>, dim3((unsigned)((p.s * p.H + 255) / 256)), dim3(256),
+                       0, st, w.dO, Ob, HD, w.dvec, (int)p.s, (int)p.H, (int)p.D);
+    BPT_TRY(check_launch("attn_dvec"));
+    }
+    for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
+      const int64_t hq0 = ch * p.U, hk0 = hq0 / p.G;
+      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
+      BPT_TRY(fill(st, w.dqacc, p.s * p.U * p.D, 0.f));
+      T* dK = w.dqkv + p.U * p.D;
+      T* dV = w.dqkv + (p.U + p.nkvc) * p.D;
+      BPT_TRY(attn_bwd<T>(st, p, w.q, w.k, w.v, w.dO + hq0 * p.D, Lb + hq0 * p.s,
+                          w.dvec + hq0 * p.s, w.dqacc, dK, dV, w.rope));
+      {
+        const int64_t n = p.s * (p.U * p.D / 2);
+        TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+        hipLaunchKernelGGL(dq_finalize_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           st, w.dqacc, p.U * p.D, w.dqkv, p.chunk_cols, w.rope, (int)p.s,
+                           (int)(p.U * p.D), (int)p.D);
+        BPT_TRY(check_launch("dq_finalize"));
+      }
+      const int64_t segc[3] = {0, p.U * p.D, (p.U + p.nkvc) * p.D};
+      const int64_t wcol[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
+      const int64_t wid[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};
+      for (int seg = 0; seg < 3; ++seg) {
+        const T* dseg = w.dqkv + segc[seg];
+        if (dwqkv) {
+          EpiOut<T, float> e{dwqkv + wcol[seg], p.qkv_cols, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, dseg, p.chunk_cols, p.h, wid[seg], p.s, e,
+                                         "dWqkv")));
+        }
+        BPT_TRY(colsum<T>(st, dseg, p.chunk_cols, p.s, wid[seg], w.part,
+                          dbqkv ? dbqkv + wcol[seg] : nullptr));
+        EpiOut<T, float> e{w.dxn, p.h, nullptr, 1.f, (ch == 0 && seg == 0) ? 0 : 1};
+        BPT_TRY((gemm<T, true, true>(st, dseg, p.chunk_cols, wqkv + wcol[seg], p.qkv_cols, p.s, p.h,
+                                     wid[seg], e, "dxn")));
+      }
+    }
+    // ---- Norm1 backward + residual: dx = dh + Norm1'(dxn)
+    BPT_TRY((norm_bwd<T, T, float>(st, p, w.dxn, p.h, xb, p.h, g1, w.dh, p.h, nullptr, dxb, p.h,
+                                   p.s, dg1, dsh1, w.npart_g, w.npart_b)));
+  }
+  return BPT_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+bpt_status check_weights(const Plan& p, const bpt_layer_weights* w) {
+  if (!w) return fail(BPT_EINVAL, "weights is NULL");
+  const void* mats[4] = {w->w_qkv, w->w_o, w->w_1, w->w_2};
+  for (const void* m : mats)
+    if (!m || !aligned16(m)) return fail(BPT_EINVAL, "weight matrix NULL or not 16-byte aligned");
+  if (p.ffn == BPT_SWIGLU && (!w->w_3 || !aligned16(w->w_3)))
+    return fail(BPT_EINVAL, "SwiGLU needs w_3 (16-byte aligned)");
+  if (!w->n1_g || !w->n2_g) return fail(BPT_EINVAL, "norm scales n1_g and n2_g are required");
+  if (p.norm == BPT_RMSNORM && (w->n1_b || w->n2_b))
+    return fail(BPT_EINVAL, "RMSNorm takes no shift (n1_b, n2_b must be NULL)");
+  const void* vecs[8] = {w->b_qkv, w->b_o, w->b_1, w->b_2, w->n1_g, w->n1_b, w->n2_g, w->n2_b};
+  for (const void* v : vecs)
+    if (v && ((uintptr_t)v % p.esz) != 0) return fail(BPT_EINVAL, "vector parameter misaligned");
+  return BPT_OK;
+}
+
+}  // namespace
+
+// ================================================================= C ABI
+extern "C" {
+
+bpt_status bpt_layer_validate(const bpt_layer_desc* desc) {
+  Plan p;
+  return make_plan(desc, p);
+}
+
+size_t bpt_layer_saved_size(const bpt_layer_desc* desc) {
+  Plan p;
+  if (make_plan(desc, p) != BPT_OK) return 0;
+  return saved_bytes(p);
+}
+
+size_t bpt_layer_workspace_size(const bpt_layer_desc* desc, int32_t backward) {
+  Plan p;
+  if (make_plan(desc, p) != BPT_OK) return 0;
+  return backward ? bwd_ws_bytes(p) : fwd_ws_bytes(p);
+}
+
+bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x, const bpt_layer_weights* w,
+                             void* y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan p;
+  BPT_TRY(make_plan(desc, p));
+  BPT_TRY(check_weights(p, w));
+  if (!x || !y || !saved || !ws) return fail(BPT_EINVAL, "x, y, saved and ws must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(saved) || ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "x, y, saved must be 16-byte and ws 256-byte aligned");
+  if (ws_bytes < fwd_ws_bytes(p)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return forward_impl<bf16>(p, (const bf16*)x, w, (bf16*)y, saved, ws, st);
+  return forward_impl<float>(p, (const float*)x, w, (float*)y, saved, ws, st);
+}
+
+bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x, const bpt_layer_weights* w,
+                              const void* saved, const void* dy, void* dx,
+                              const bpt_layer_grads* grads, void* ws, size_t ws_bytes,
+                              void* stream) {
+  g_last_error.clear();
+  Plan p;
+  BPT_TRY(make_plan(desc, p));
+  BPT_TRY(check_weights(p, w));
+  if (!grads) return fail(BPT_EINVAL, "grads is NULL");
+  if (grads->accumulate != 0 && grads->accumulate != 1)
+    return fail(BPT_EINVAL, "grads->accumulate must be 0 or 1");
+  if (!x || !saved || !dy || !dx || !ws)
+    return fail(BPT_EINVAL, "x, saved, dy, dx and ws must be non-NULL");
+  if (!aligned16(x) || !aligned16(saved) || !aligned16(dy) || !aligned16(dx) || ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "x, saved, dy, dx must be 16-byte and ws 256-byte aligned");
+  const float* gp[13] = {grads->dw_qkv, grads->db_qkv, grads->dw_o, grads->db_o, grads->dw_1,
+                         grads->db_1, grads->dw_2, grads->db_2, grads->dw_3, grads->dn1_g,
+                         grads->dn1_b, grads->dn2_g, grads->dn2_b};
+  for (const float* g : gp)
+    if (g && ((uintptr_t)g & 3)) return fail(BPT_EINVAL, "gradient buffer misaligned");
+  if (ws_bytes < bwd_ws_bytes(p)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return backward_impl<bf16>(p, (const bf16*)x, w, saved, (const bf16*)dy, (bf16*)dx, grads, ws,
+                               st);
+  return backward_impl<float>(p, (const float*)x, w, saved, (const float*)dy, (float*)dx, grads, ws,
+                              st);
+}
+
+const char* bpt_status_string(bpt_status s) {
+  switch (s) {
+    case BPT_OK: return "ok";
+    case BPT_EINVAL: return "invalid argument";
+    case BPT_EWORKSPACE: return "workspace too small";
+    case BPT_EUNSUPPORTED: return "unsupported configuration";
+    case BPT_EHIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* bpt_last_error(void) { return g_last_error.c_str(); }
+
+bpt_status bpt_timing_enable(uint32_t class_mask) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.mask = class_mask & ((1u << BPT_KERNEL_CLASSES) - 1);
+  return BPT_OK;
+}
+
+bpt_status bpt_timing_read(double* total_ms, int64_t* launches, int32_t reset) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  bpt_status st = BPT_OK;
+  for (auto& r : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = fail(BPT_EHIP, "timing event query failed");
+    t.ms[r.cls] += ms;
+    t.n[r.cls] += 1;
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  for (int c = 0; c < BPT_KERNEL_CLASSES; ++c) {
+    if (total_ms) total_ms[c] = t.ms[c];
+    if (launches) launches[c] = t.n[c];
+    if (reset) { t.ms[c] = 0.0; t.n[c] = 0; }
+  }
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,302 @@
+// MFMA GEMM for gfx950 with fused epilogues.
+//
+//   C[m, n] = sum_k A(m, k) * B(n, k)          (fp32 accumulation)
+//
+// Operand storage (row-major in memory):
+//   A_KMAJ: A(m, k) = A[m * lda + k]   (activations, K contiguous)
+//   else  : A(m, k) = A[k * lda + m]   (M contiguous; e.g. X^T for dW = X^T dY)
+//   B_KMAJ: B(n, k) = B[n * ldb + k]   (e.g. W for dX = dY W^T)
+//   else  : B(n, k) = B[k * ldb + n]   (e.g. a weight [in, out] for y = x W)
+//
+// Tiles are staged in LDS K-contiguous (padded by 16 B per row). An
+// MN-contiguous operand is loaded as 4(k) x 8(m) bf16 sub-blocks with 16-byte
+// global loads and transposed in registers before the LDS store, so every
+// layout the layer needs (forward x W, backward dY W^T and X^T dY) runs on the
+// same MFMA inner loop without separate transpose passes.
+//
+// Workgroup: 256 threads = 2 x 2 waves; each wave owns a (BM/2) x (BN/2)
+// block of 32x32 MFMA tiles. Global loads of the next K step are issued before
+// the current step's MFMAs (register prefetch, LDS double buffer).
+#pragma once
+
+#include "device_common.hpp"
+
+namespace bpt {
+
+// ----------------------------------------------------------------- activations
+__device__ __forceinline__ float act_relu(float a) { return a > 0.f ? a : 0.f; }
+__device__ __forceinline__ float act_gelu(float a) {
+  return 0.5f * a * (1.f + erff(a * 0.70710678118654752f));
+}
+__device__ __forceinline__ float act_gelu_grad(float a) {
+  float cdf = 0.5f * (1.f + erff(a * 0.70710678118654752f));
+  float pdf = 0.39894228040143268f * expf(-0.5f * a * a);
+  return cdf + a * pdf;
+}
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.f / (1.f + expf(-a)); }
+
+enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
+
+// ----------------------------------------------------------------- epilogues
+// Each epilogue is called once per in-bounds output element with the fp32
+// accumulator value v (and, when kPair, the value of column n ^ 1 in the same
+// row, used by the RoPE rotation).
+
+// out = alpha * v (+ bias[n]) (+ out if accumulate)
+template <typename T, typename OutT>
+struct EpiOut {
+  OutT* out; int64_t ldo; const T* bias; float alpha; int accumulate;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    float r = alpha * v;
+    if (bias) r += to_f32(bias[n]);
+    OutT* p = out + (int64_t)m * ldo + n;
+    if (accumulate) r += to_f32(*p);
+    *p = from_f32<OutT>(r);
+  }
+};
+
+// Q/K/V projection: + bias, optional RoPE on interleaved pairs, scattered to a
+// head-major [heads, s, D] buffer.
+template <typename T>
+struct EpiQKV {
+  T* out; int64_t head_stride; int D; const T* bias; const float2* rope; int row0;
+  static constexpr bool kPair = true;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float vp) const {
+    if (bias) { v += to_f32(bias[n]); vp += to_f32(bias[n ^ 1]); }
+    const int head = n / D, dd = n - head * D;
+    if (rope) {
+      float2 cs = rope[(int64_t)(row0 + m) * (D / 2) + (dd >> 1)];
+      v = (dd & 1) ? (vp * cs.y + v * cs.x) : (v * cs.x - vp * cs.y);
+    }
+    out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
+  }
+};
+
+// out = v + bias[n] + res[m, n]
+template <typename T, typename ResT, typename OutT>
+struct EpiResid {
+  OutT* out; int64_t ldo; const ResT* res; int64_t ldr; const T* bias;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    if (bias) v += to_f32(bias[n]);
+    v += to_f32(res[(int64_t)m * ldr + n]);
+    out[(int64_t)m * ldo + n] = from_f32<OutT>(v);
+  }
+};
+
+// a = v + bias[n]; optionally keep a; u = act(a)
+template <typename T>
+struct EpiAct {
+  T* u; T* a_keep; int64_t ldo; const T* bias; int act;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    if (bias) v += to_f32(bias[n]);
+    const int64_t i = (int64_t)m * ldo + n;
+    if (a_keep) a_keep[i] = from_f32<T>(v);
+    u[i] = from_f32<T>(act == ACT_RELU ? act_relu(v) : act_gelu(v));
+  }
+};
+
+// SwiGLU up projection: u = silu(gate[m, n]) * v; optionally keep v.
+template <typename T>
+struct EpiSwiUp {
+  T* u; T* up_keep; const T* gate; int64_t ldo;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    const int64_t i = (int64_t)m * ldo + n;
+    if (up_keep) up_keep[i] = from_f32<T>(v);
+    float g = to_f32(gate[i]);
+    u[i] = from_f32<T>(g * sigmoidf_(g) * v);
+  }
+};
+
+// da = v * act'(a[m, n])
+template <typename T>
+struct EpiActGrad {
+  T* da; const T* a; int64_t ldo; int act;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    const int64_t i = (int64_t)m * ldo + n;
+    float x = to_f32(a[i]);
+    float gr = act == ACT_RELU ? (x > 0.f ? 1.f : 0.f) : act_gelu_grad(x);
+    da[i] = from_f32<T>(v * gr);
+  }
+};
+
+// SwiGLU backward from du = v: d gate = du * up * s(g) (1 + g (1 - s(g))),
+// d up = du * g * s(g).
+template <typename T>
+struct EpiSwiGrad {
+  T* dgate; T* dup; const T* gate; const T* up; int64_t ldo;
+  static constexpr bool kPair = false;
+  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+    const int64_t i = (int64_t)m * ldo + n;
+    float g = to_f32(gate[i]), u = to_f32(up[i]);
+    float sg = sigmoidf_(g);
+    dgate[i] = from_f32<T>(v * u * sg * (1.f + g * (1.f - sg)));
+    dup[i] = from_f32<T>(v * g * sg);
+  }
+};
+
+// ----------------------------------------------------------------- tile loaders
+// Loads one operand tile (R rows x BK reduction) into registers and stores it
+// K-contiguous into LDS. Per thread: 4 vector loads of 16 bytes.
+template <typename T, bool KMAJ, int R, int BK>
+struct TileLoader {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int LDK = BK + VEC;
+  static constexpr int N_LOADS = 4;
+  static_assert(R * BK / VEC == 4 * 256, "tile must be 4 x 16 B per thread");
+  u32x4 reg[4];
+
+  // rows [row0, row0 + R) of limit rlim; reduction [k0, k0 + BK) of limit K
+  __device__ __forceinline__ void load(const T* __restrict__ src, int64_t ldm, int row0, int rlim,
+                                       int k0, int K, int tid) {
+    if constexpr (KMAJ) {
+      constexpr int CPR = BK / VEC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int r = c / CPR, kc = (c % CPR) * VEC;
+        const int gr = row0 + r, gk = k0 + kc;
+        if (gr < rlim && gk < K) reg[i] = ld<u32x4>(src + (int64_t)gr * ldm + gk);
+        else reg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      constexpr int KB = BK / 4;
+      const int kb = tid % KB, rb = tid / KB;
+      const int gr = row0 + rb * VEC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gk = k0 + 4 * kb + i;
+        if (gr < rlim && gk < K) reg[i] = ld<u32x4>(src + (int64_t)gk * ldm + gr);
+        else reg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(T* tile, int tid) const {
+    if constexpr (KMAJ) {
+      constexpr int CPR = BK / VEC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int r = c / CPR, kc = (c % CPR) * VEC;
+        st<u32x4>(tile + r * LDK + kc, reg[i]);
+      }
+    } else {
+      constexpr int KB = BK / 4;
+      const int kb = tid % KB, rb = tid / KB;
+      if constexpr (sizeof(T) == 2) {
+        u32x2 out[8];
+        transpose_4xvec(reg, out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st<u32x2>(tile + (rb * 8 + j) * LDK + 4 * kb, out[j]);
+      } else {
+        u32x4 out[4];
+        transpose_4xvec(reg, out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st<u32x4>(tile + (rb * 4 + j) * LDK + 4 * kb, out[j]);
+      }
+    }
+  }
+};
+
+// ----------------------------------------------------------------- kernel
+template <typename T, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, class Epi>
+__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int64_t lda,
+                                                   const T* __restrict__ B, int64_t ldb, int M,
+                                                   int N, int K, Epi epi) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int LDK = BK + VEC;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LDK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, g = lane >> 5;
+
+  // Tile order: each XCD (workgroups are dealt round-robin over 8) owns a
+  // contiguous range of tiles, walked in groups of 8 tile-rows so the
+  // workgroups resident on one XCD share A and B tiles in its L2.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int nt = tiles_m * tiles_n;
+  int tile;
+  {
+    const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+    const int q = nt >> 3, rem = nt & 7;
+    tile = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
+  }
+  constexpr int GROUP = 8;
+  const int group = tile / (GROUP * tiles_n);
+  const int first_m = group * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (tile % (GROUP * tiles_n)) % gsz;
+  const int tn = (tile % (GROUP * tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
+
+  TileLoader<T, A_KMAJ, BM, BK> la;
+  TileLoader<T, B_KMAJ, BN, BK> lb;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+
+  const int nk = (K + BK - 1) / BK;
+  if (nk > 0) {
+    la.load(A, lda, m0, M, 0, K, tid);
+    lb.load(B, ldb, n0, N, 0, K, tid);
+    la.store(smem[0], tid);
+    lb.store(smem[0] + BM * LDK, tid);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      la.load(A, lda, m0, M, (kt + 1) * BK, K, tid);
+      lb.load(B, ldb, n0, N, (kt + 1) * BK, K, tid);
+    }
+    const T* As = smem[buf];
+    const T* Bs = smem[buf] + BM * LDK;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      typename Frag<T>::type af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = ld_frag(As + (wm0 + 32 * i + lr) * LDK + 16 * kk + 8 * g);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = ld_frag(Bs + (wn0 + 32 * j + lr) * LDK + 16 * kk + 8 * g);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) {
+      la.store(smem[buf ^ 1], tid);
+      lb.store(smem[buf ^ 1] + BM * LDK, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn0 + 32 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm0 + 32 * i + acc_row(r, g);
+        float v = acc[i][j][r];
+        float vp = 0.f;
+        if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
+        if (row < M && col < N) epi(row, col, v, vp);
+      }
+    }
+}
+
+}  // namespace bpt

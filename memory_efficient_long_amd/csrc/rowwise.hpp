@@ -1,0 +1,271 @@
+// Row-wise and reduction kernels of the layer: LayerNorm / RMSNorm forward and
+// backward (one wave per row, statistics in fp32), column sums for bias and
+// norm-parameter gradients (deterministic two-stage), the RoPE cos/sin table,
+// the attention-backward row term D = rowsum(dO * O), and the dQ finaliser.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace bpt {
+
+__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
+  bf16x8 x = ld<bf16x8>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  f32x4 a = ld<f32x4>(p), b = ld<f32x4>(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (bf16)v[e];
+  st<bf16x8>(p, x);
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  st<f32x4>(p, f32x4{v[0], v[1], v[2], v[3]});
+  st<f32x4>(p + 4, f32x4{v[4], v[5], v[6], v[7]});
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+enum NormKind { NORM_LAYER = 0, NORM_RMS = 1 };
+
+// out = Norm(x) * gamma (+ beta). NCH: 8-element chunks per lane (h <= 512 * NCH).
+template <typename T, typename Tin, typename Tout, int NCH>
+__global__ __launch_bounds__(256) void norm_fwd_kernel(const Tin* __restrict__ x, int64_t ldx,
+                                                       const T* __restrict__ gamma,
+                                                       const T* __restrict__ beta, Tout* out,
+                                                       int64_t ldo, int rows, int h, int kind,
+                                                       float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nch = h / 8;
+  float v[NCH][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      load8(x + (int64_t)row * ldx + 8 * c, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += v[i][e];
+    }
+  }
+  const float inv_h = 1.f / (float)h;
+  float mean = 0.f;
+  if (kind == NORM_LAYER) mean = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    if (lane + 64 * i < nch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[i][e] - mean;
+        sq += d * d;
+      }
+  const float rstd = 1.f / sqrtf(wave_sum(sq) * inv_h + eps);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = (v[i][e] - mean) * rstd * to_f32(gamma[8 * c + e]);
+        if (beta) y += to_f32(beta[8 * c + e]);
+        o[e] = y;
+      }
+      store8(out + (int64_t)row * ldo + 8 * c, o);
+    }
+  }
+}
+
+// Norm backward fused with the residual:
+//   out = res + rstd * (gx - [mean(gx)] - xhat * mean(gx * xhat)),  gx = dz * gamma
+// (the bracketed term only for LayerNorm). Rows are strided over the grid's
+// waves; each wave keeps fp32 partial sums of dz * xhat and dz for the scale
+// and shift gradients and writes them to part_g / part_b [total waves, h].
+template <typename T, typename Tin, typename Tres, int NCH>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(
+    const float* __restrict__ dz, int64_t lddz, const Tin* __restrict__ xin, int64_t ldx,
+    const T* __restrict__ gamma, const Tres* __restrict__ res, int64_t ldr, float* out_f,
+    T* out_t, int64_t ldo, float* part_g, float* part_b, int rows, int h, int kind, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  const int nch = h / 8;
+  const float inv_h = 1.f / (float)h;
+  float pg[NCH][8], pb[NCH][8];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { pg[i][e] = 0.f; pb[i][e] = 0.f; }
+
+  for (int row = wave; row < rows; row += nwaves) {
+    float xv[NCH][8], gv[NCH][8];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        load8(xin + (int64_t)row * ldx + 8 * c, xv[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += xv[i][e];
+      }
+    }
+    float mean = 0.f;
+    if (kind == NORM_LAYER) mean = wave_sum(sum) * inv_h;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nch)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = xv[i][e] - mean;
+          sq += d * d;
+        }
+    const float rstd = 1.f / sqrtf(wave_sum(sq) * inv_h + eps);
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        float dzv[8];
+        load8(dz + (int64_t)row * lddz + 8 * c, dzv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xh = (xv[i][e] - mean) * rstd;
+          xv[i][e] = xh;
+          const float gx = dzv[e] * to_f32(gamma[8 * c + e]);
+          gv[i][e] = gx;
+          s1 += gx;
+          s2 += gx * xh;
+          pg[i][e] += dzv[e] * xh;
+          pb[i][e] += dzv[e];
+        }
+      }
+    }
+    const float m1 = kind == NORM_LAYER ? wave_sum(s1) * inv_h : 0.f;
+    const float m2 = wave_sum(s2) * inv_h;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) {
+        float rv[8], o[8];
+        load8(res + (int64_t)row * ldr + 8 * c, rv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = rv[e] + rstd * (gv[i][e] - m1 - xv[i][e] * m2);
+        if (out_f) store8(out_f + (int64_t)row * ldo + 8 * c, o);
+        if (out_t) store8(out_t + (int64_t)row * ldo + 8 * c, o);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      if (part_g) store8(part_g + (int64_t)wave * h + 8 * c, pg[i]);
+      if (part_b) store8(part_b + (int64_t)wave * h + 8 * c, pb[i]);
+    }
+  }
+}
+
+// Stage 1 of a column sum over X [rows, N]: grid (ceil(N / 64), P); block
+// (64 columns x 4 row lanes); part[blockIdx.y, col] = sum over the block's rows.
+template <typename Tin>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restrict__ X, int64_t ldx,
+                                                             int rows, int N, float* part) {
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
+  const int per = (rows + gridDim.y - 1) / gridDim.y;
+  const int r0 = blockIdx.y * per, r1 = min(rows, r0 + per);
+  float acc = 0.f;
+  if (col < N)
+    for (int r = r0 + rl; r < r1; r += 4) acc += to_f32(X[(int64_t)r * ldx + col]);
+  red[rl][cl] = acc;
+  __syncthreads();
+  if (rl == 0 && col < N)
+    part[(int64_t)blockIdx.y * N + col] = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+}
+
+// Stage 2: out[col] (+)= sum_p part[p, col].
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int P,
+                                                           int N, float* out, int accumulate) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= N) return;
+  float acc = 0.f;
+  for (int p = 0; p < P; ++p) acc += part[(int64_t)p * N + col];
+  out[col] = accumulate ? out[col] + acc : acc;
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// RoPE table: tab[p, i] = (cos, sin)(p * base^(-2i/D)), angles in fp64.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int s, int D, double base) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int half = D / 2;
+  if (idx >= (int64_t)s * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double theta = pow(base, -2.0 * (double)i / (double)D);
+  const double ang = (double)p * theta;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// D[h, q] = sum_d dO[q, h D + d] * O[q, h D + d] (fp32), one thread per (row, head).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_dvec_kernel(const T* __restrict__ dout,
+                                                        const T* __restrict__ o, int64_t ld,
+                                                        float* dvec, int s, int nh, int D) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)s * nh) return;
+  const int row = (int)(t / nh), h = (int)(t % nh);
+  const T* a = dout + (int64_t)row * ld + (int64_t)h * D;
+  const T* b = o + (int64_t)row * ld + (int64_t)h * D;
+  float acc = 0.f;
+  for (int c = 0; c < D; c += 8) {
+    float va[8], vb[8];
+    load8(a + c, va);
+    load8(b + c, vb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += va[e] * vb[e];
+  }
+  dvec[(int64_t)h * s + row] = acc;
+}
+
+// dQ fp32 accumulator [s, ncols] -> storage dtype, with the inverse RoPE
+// rotation of each pair (2i, 2i+1) at the row's position.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ dq, int64_t lddq,
+                                                          T* out, int64_t ldo,
+                                                          const float2* __restrict__ rope, int s,
+                                                          int ncols, int D) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int pairs = ncols / 2;
+  if (t >= (int64_t)s * pairs) return;
+  const int row = (int)(t / pairs), pc = (int)(t % pairs);
+  const int col = 2 * pc;
+  float e = dq[(int64_t)row * lddq + col], o = dq[(int64_t)row * lddq + col + 1];
+  if (rope) {
+    const float2 cs = rope[(int64_t)row * (D / 2) + (col % D) / 2];
+    const float e2 = e * cs.x + o * cs.y;
+    const float o2 = -e * cs.y + o * cs.x;
+    e = e2;
+    o = o2;
+  }
+  out[(int64_t)row * ldo + col] = from_f32<T>(e);
+  out[(int64_t)row * ldo + col + 1] = from_f32<T>(o);
+}
+
+}  // namespace bpt

@@ -1,0 +1,188 @@
+"""Host-side tests of the C ABI (no GPU work is launched).
+
+* libbpt.so loads and exports every function include/bpt.h declares.
+* The ctypes mirrors of the structs match the C layout (sizeof / offsetof from
+  a small program compiled with gcc against the header).
+* Descriptor validation returns the documented status before any launch.
+* saved and workspace sizes are affine in s and hold no s * ffn_dim term.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import memory_efficient_long_amd as bpt
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpt.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bpt_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = bpt.load_library()
+    names = _declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bpt.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bpt_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "bpt.h"
+#define F(S, m) printf(#S "." #m " %zu\n", offsetof(S, m));
+int main(void) {
+  printf("desc %zu\nweights %zu\ngrads %zu\n", sizeof(bpt_layer_desc),
+         sizeof(bpt_layer_weights), sizeof(bpt_layer_grads));
+  F(bpt_layer_desc, batch) F(bpt_layer_desc, head_chunk) F(bpt_layer_desc, rope_base)
+  F(bpt_layer_desc, norm_eps) F(bpt_layer_grads, accumulate) F(bpt_layer_weights, n2_b)
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    lines = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], capture_output=True,
+                                                          text=True, check=True).stdout.split("\n")
+                 if l)
+    assert int(lines["desc"]) == ctypes.sizeof(bpt.BptLayerDesc)
+    assert int(lines["weights"]) == ctypes.sizeof(bpt.BptLayerWeights)
+    assert int(lines["grads"]) == ctypes.sizeof(bpt.BptLayerGrads)
+    for key, (cls, field) in {"bpt_layer_desc.batch": (bpt.BptLayerDesc, "batch"),
+                              "bpt_layer_desc.head_chunk": (bpt.BptLayerDesc, "head_chunk"),
+                              "bpt_layer_desc.rope_base": (bpt.BptLayerDesc, "rope_base"),
+                              "bpt_layer_desc.norm_eps": (bpt.BptLayerDesc, "norm_eps"),
+                              "bpt_layer_grads.accumulate": (bpt.BptLayerGrads, "accumulate"),
+                              "bpt_layer_weights.n2_b": (bpt.BptLayerWeights, "n2_b")}.items():
+        assert int(lines[key]) == getattr(cls, field).offset, key
+
+
+def _desc(name="gpt1b-s8k", **kw):
+    d = bpt.LayerConfig.from_shape(wl.WORKLOADS[name]).desc()
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS) + list(wl.SMALL))
+def test_workloads_validate(name):
+    sh = wl.WORKLOADS.get(name) or wl.SMALL[name]
+    d = bpt.LayerConfig.from_shape(sh).desc()
+    assert bpt.bpt_layer_validate(d) == 0, bpt.bpt_last_error()
+    assert bpt.bpt_layer_saved_size(d) > 0
+    assert bpt.bpt_layer_workspace_size(d, False) > 0
+    assert bpt.bpt_layer_workspace_size(d, True) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 2, 1), ("dtype", 7, 1), ("norm", 3, 1), ("ffn", 9, 1), ("causal", 2, 1),
+    ("seq_len", 8200, 1), ("seq_len", 0, 1), ("hidden", 2000, 1), ("n_kv_heads", 3, 1),
+    ("head_dim", 96, 3), ("ffn_dim", 100, 1), ("q_block", 1000, 1), ("kv_block", 3000, 1),
+    ("head_chunk", 3, 1), ("head_chunk", 0, 1), ("norm_eps", float("nan"), 1),
+])
+def test_invalid_descriptors(field, value, status):
+    d = _desc(**{field: value})
+    assert bpt.bpt_layer_validate(d) == status
+    assert bpt.bpt_last_error()
+    assert bpt.bpt_layer_saved_size(d) == 0
+    assert bpt.bpt_layer_workspace_size(d, True) == 0
+
+
+def test_gqa_head_chunk_rule():
+    # head_chunk must hold whole GQA groups (32 query / 8 KV heads: group 4).
+    assert bpt.bpt_layer_validate(_desc("llama8b-s64k", head_chunk=4)) == 0
+    assert bpt.bpt_layer_validate(_desc("llama8b-s64k", head_chunk=2)) == 1
+    assert bpt.bpt_layer_validate(_desc("gpt-tiny-fp32", head_dim=64, hidden=128)) == 0
+    assert bpt.bpt_layer_validate(_desc("gpt-tiny-fp32", head_dim=128, hidden=256)) == 3
+
+
+def test_forward_backward_reject_bad_arguments_before_launch():
+    lib = bpt.load_library()
+    d = _desc()
+    w = bpt.BptLayerWeights(w_qkv=0x1000, w_o=0x1000, w_1=0x1000, w_2=0x1000, n1_g=0x1000,
+                            n2_g=0x1000)
+    ws_need = bpt.bpt_layer_workspace_size(d, False)
+    fake = 0x10000
+    # NULL x
+    assert lib.bpt_layer_forward(ctypes.byref(d), None, ctypes.byref(w), fake, fake, fake,
+                                 ws_need, None) == 1
+    # misaligned y
+    assert lib.bpt_layer_forward(ctypes.byref(d), fake, ctypes.byref(w), fake + 2, fake, fake,
+                                 ws_need, None) == 1
+    # workspace too small
+    assert lib.bpt_layer_forward(ctypes.byref(d), fake, ctypes.byref(w), fake, fake, fake,
+                                 ws_need - 1, None) == 2
+    # missing weight matrix
+    w2 = bpt.BptLayerWeights(w_qkv=0x1000, w_o=None, w_1=0x1000, w_2=0x1000, n1_g=0x1000,
+                             n2_g=0x1000)
+    assert lib.bpt_layer_forward(ctypes.byref(d), fake, ctypes.byref(w2), fake, fake, fake,
+                                 ws_need, None) == 1
+    # RMSNorm with a shift
+    dr = _desc("llama8b-s64k")
+    wr = bpt.BptLayerWeights(w_qkv=0x1000, w_o=0x1000, w_1=0x1000, w_2=0x1000, w_3=0x1000,
+                             n1_g=0x1000, n2_g=0x1000, n1_b=0x1000)
+    assert lib.bpt_layer_forward(ctypes.byref(dr), fake, ctypes.byref(wr), fake, fake, fake,
+                                 bpt.bpt_layer_workspace_size(dr, False), None) == 1
+    # backward: NULL grads table, bad accumulate flag, small workspace
+    wsb = bpt.bpt_layer_workspace_size(d, True)
+    assert lib.bpt_layer_backward(ctypes.byref(d), fake, ctypes.byref(w), fake, fake, fake, None,
+                                  fake, wsb, None) == 1
+    g = bpt.BptLayerGrads(accumulate=5)
+    assert lib.bpt_layer_backward(ctypes.byref(d), fake, ctypes.byref(w), fake, fake, fake,
+                                  ctypes.byref(g), fake, wsb, None) == 1
+    g = bpt.BptLayerGrads(accumulate=0)
+    assert lib.bpt_layer_backward(ctypes.byref(d), fake, ctypes.byref(w), fake, fake, fake,
+                                  ctypes.byref(g), fake, wsb - 256, None) == 2
+    assert bpt.bpt_status_string(2) == "workspace too small"
+
+
+@pytest.mark.parametrize("backward", [False, True])
+def test_memory_is_affine_in_s_without_s_times_ffn(backward):
+    base = wl.WORKLOADS["gpt1b-s128k"]
+
+    def ws(s, f):
+        d = bpt.LayerConfig.from_shape(base.replace(seq_len=s, ffn_dim=f)).desc()
+        return bpt.bpt_layer_workspace_size(d, backward), bpt.bpt_layer_saved_size(d)
+
+    sizes = [ws(s, 8192) for s in (16384, 32768, 65536, 131072)]
+    for i in range(2):
+        assert [sizes[j][i] for j in range(4)] == sorted(sizes[j][i] for j in range(4))
+        d1 = sizes[1][i] - sizes[0][i]
+        d2 = (sizes[2][i] - sizes[1][i]) / 2
+        d3 = (sizes[3][i] - sizes[2][i]) / 4
+        assert abs(d1 - d2) <= 4096 and abs(d2 - d3) <= 4096     # linear in s (alignment slack)
+    # The FFN width changes the workspace by the same amount at every s: the
+    # FFN scratch is q_block x ffn_dim, never s x ffn_dim.
+    df_small = ws(16384, 16384)[0] - ws(16384, 8192)[0]
+    df_large = ws(131072, 16384)[0] - ws(131072, 8192)[0]
+    assert df_small == df_large
+    # Saved state is exactly O (bf16) plus one fp32 LSE per row and head.
+    sh = base
+    assert sizes[3][1] == sh.seq_len * sh.n_heads * sh.head_dim * 2 + sh.n_heads * sh.seq_len * 4
+
+
+def test_weight_set_matches_printed_parameter_counts(repo_root):
+    """12h^2 + 13h per GPT layer ("Training memory", §3 parameters and §4/§5
+    printed values)."""
+    import json
+    gold = json.load(open(os.path.join(repo_root, "tests", "golden", "page3_printed_values.json")))
+    for h, count in gold["params_per_gpt_layer"].items():
+        h = int(h)
+        sh = wl.WORKLOADS["gpt1b-s8k"].replace(hidden=h, n_heads=h // 128, n_kv_heads=h // 128,
+                                               head_dim=min(128, h), ffn_dim=4 * h)
+        n = sum(int(__import__("numpy").prod(s)) for s in wl.weight_shapes(sh).values())
+        assert n == count == 12 * h * h + 13 * h

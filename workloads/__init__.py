@@ -210,11 +210,14 @@ def make_dy(sh: LayerShape, rows: Optional[np.ndarray] = None) -> Tensor:
 
 def sample_rows(sh: LayerShape, n_head: int = 8, n_tail: int = 8, n_mid: int = 8,
                 seed: int = 7) -> np.ndarray:
-    """Sequence positions sampled for full-size checks: the first rows, the last
-    rows (longest causal key range) and random rows in between."""
+    """Sequence positions sampled for full-size checks: the first rows, rows
+    just before the end (longest causal key range; the very last row is left
+    out so a causal layer's last position must receive exactly zero gradient)
+    and random rows in between."""
     s = sh.seq_len
     rng = np.random.default_rng(1000 * sh.wid + seed)
-    mid = rng.choice(np.arange(n_head, s - n_tail), size=min(n_mid, max(0, s - n_head - n_tail)),
+    tail0 = max(n_head, s - 1 - n_tail)
+    mid = rng.choice(np.arange(n_head, tail0), size=min(n_mid, max(0, tail0 - n_head)),
                      replace=False)
-    rows = np.concatenate([np.arange(min(n_head, s)), mid, np.arange(max(0, s - n_tail), s)])
+    rows = np.concatenate([np.arange(min(n_head, s)), mid, np.arange(tail0, s - 1)])
     return np.unique(rows)
