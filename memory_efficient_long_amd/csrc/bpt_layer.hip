@@ -91,7 +91,7 @@ struct TimedLaunch {
 };
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
-constexpr int kNormWaves = 1024;   // waves of the norm backward (partial rows)
+constexpr int kNormWaves = 256;    // waves of the norm backward (partial rows)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -186,7 +186,7 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
 template <typename T>
 struct BwdWs {
   T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t;
-  float *dvec, *dh, *dxn, *dqacc, *h1, *dz, *part, *npart_g, *npart_b;
+  float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b;
   float2* rope;
 };
 
@@ -203,7 +203,6 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.q = c.take<T>(p.U * p.s * p.D);
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
-  w.dqacc = c.take<float>(p.s * p.U * p.D);
   w.dqkv = c.take<T>(p.s * p.chunk_cols);
   w.h1 = c.take<float>(p.cq * p.h);
   w.z = c.take<T>(p.cq * p.h);
@@ -295,7 +294,7 @@ bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz
 #undef NB
   BPT_TRY(check_launch("norm_bwd"));
   const int P = nblk * 4;
-  const dim3 g2((unsigned)((p.h + 255) / 256));
+  const dim3 g2((unsigned)((p.h + 63) / 64));
   if (dg) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pg, P, (int)p.h, dg, 1);
   if (db) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pb, P, (int)p.h, db, 1);
   return check_launch("norm_bwd reduce");
@@ -310,7 +309,7 @@ bpt_status colsum(hipStream_t st, const Tin* X, int64_t ldx, int64_t rows, int64
   TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
   hipLaunchKernelGGL(colsum_partial_kernel<Tin>, dim3((unsigned)((N + 63) / 64), P), dim3(256), 0,
                      st, X, ldx, (int)rows, (int)N, part);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
                      part, P, (int)N, out, 1);
   return check_launch("colsum");
 }
@@ -348,25 +347,32 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
 
 template <typename T>
 bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v,
-                    const T* dout, const float* lse, const float* dvec, float* dq, T* dk, T* dv,
+                    const T* dout, const float* lse, const float* dvec, T* dq, T* dk, T* dv,
                     const float2* rope) {
   AttnBwdArgs<T> a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.lddo = p.H * p.D; a.lse = lse; a.dvec = dvec;
-  a.dq = dq; a.lddq = p.U * p.D; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
+  a.dq = dq; a.lddq = p.chunk_cols; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
   a.s = (int)p.s; a.nh = (int)p.U; a.nkv = (int)p.nkvc; a.group = (int)p.G; a.causal = p.causal;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   a.scale = (float)(1.0 / std::sqrt((double)p.D));
-  const dim3 grid((unsigned)(p.nkvc * ((p.s + 127) / 128))), blk(256);
+  const dim3 gkv((unsigned)(p.nkvc * ((p.s + 127) / 128))), gq((unsigned)(p.U * ((p.s + 127) / 128)));
+  const dim3 blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_BWD, st);
   if constexpr (sizeof(T) == 2) {
     if (p.D == 128) {
-      hipLaunchKernelGGL((attn_bwd_kernel<T, 128>), grid, blk, 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 128>), gkv, blk, 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 128>), gq, blk, 0, st, a);
       return check_launch("attn_bwd");
     }
   }
   if (p.D == 128) return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
-  if (p.D == 64) hipLaunchKernelGGL((attn_bwd_kernel<T, 64>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((attn_bwd_kernel<T, 32>), grid, blk, 0, st, a);
+  if (p.D == 64) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
+  }
   return check_launch("attn_bwd");
 }
 
@@ -553,19 +559,10 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
       const int64_t hq0 = ch * p.U, hk0 = hq0 / p.G;
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
-      BPT_TRY(fill(st, w.dqacc, p.s * p.U * p.D, 0.f));
       T* dK = w.dqkv + p.U * p.D;
       T* dV = w.dqkv + (p.U + p.nkvc) * p.D;
       BPT_TRY(attn_bwd<T>(st, p, w.q, w.k, w.v, w.dO + hq0 * p.D, Lb + hq0 * p.s,
-                          w.dvec + hq0 * p.s, w.dqacc, dK, dV, w.rope));
-      {
-        const int64_t n = p.s * (p.U * p.D / 2);
-        TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
-        hipLaunchKernelGGL(dq_finalize_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                           st, w.dqacc, p.U * p.D, w.dqkv, p.chunk_cols, w.rope, (int)p.s,
-                           (int)(p.U * p.D), (int)p.D);
-        BPT_TRY(check_launch("dq_finalize"));
-      }
+                          w.dvec + hq0 * p.s, w.dqkv, dK, dV, w.rope));
       const int64_t segc[3] = {0, p.U * p.D, (p.U + p.nkvc) * p.D};
       const int64_t wcol[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
       const int64_t wid[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};

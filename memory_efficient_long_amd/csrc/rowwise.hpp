@@ -1,7 +1,7 @@
 // Row-wise and reduction kernels of the layer: LayerNorm / RMSNorm forward and
 // backward (one wave per row, statistics in fp32), column sums for bias and
 // norm-parameter gradients (deterministic two-stage), the RoPE cos/sin table,
-// the attention-backward row term D = rowsum(dO * O), and the dQ finaliser.
+// and the attention-backward row term D = rowsum(dO * O).
 #pragma once
 
 #include "device_common.hpp"
@@ -197,14 +197,28 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restri
     part[(int64_t)blockIdx.y * N + col] = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
 }
 
-// Stage 2: out[col] (+)= sum_p part[p, col].
+// Stage 2: out[col] (+)= sum_p part[p, col]; block = 64 columns x 4 partial
+// lanes, each lane summing every 4th partial row, then an LDS reduction.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int P,
                                                            int N, float* out, int accumulate) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= N) return;
-  float acc = 0.f;
-  for (int p = 0; p < P; ++p) acc += part[(int64_t)p * N + col];
-  out[col] = accumulate ? out[col] + acc : acc;
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
+  float a0 = 0.f, a1 = 0.f;
+  if (col < N) {
+    int p = rl;
+    for (; p + 4 < P; p += 8) {
+      a0 += part[(int64_t)p * N + col];
+      a1 += part[(int64_t)(p + 4) * N + col];
+    }
+    if (p < P) a0 += part[(int64_t)p * N + col];
+  }
+  red[rl][cl] = a0 + a1;
+  __syncthreads();
+  if (rl == 0 && col < N) {
+    const float acc = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+    out[col] = accumulate ? out[col] + acc : acc;
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float v) {
@@ -242,30 +256,6 @@ __global__ __launch_bounds__(256) void attn_dvec_kernel(const T* __restrict__ do
     for (int e = 0; e < 8; ++e) acc += va[e] * vb[e];
   }
   dvec[(int64_t)h * s + row] = acc;
-}
-
-// dQ fp32 accumulator [s, ncols] -> storage dtype, with the inverse RoPE
-// rotation of each pair (2i, 2i+1) at the row's position.
-template <typename T>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ dq, int64_t lddq,
-                                                          T* out, int64_t ldo,
-                                                          const float2* __restrict__ rope, int s,
-                                                          int ncols, int D) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int pairs = ncols / 2;
-  if (t >= (int64_t)s * pairs) return;
-  const int row = (int)(t / pairs), pc = (int)(t % pairs);
-  const int col = 2 * pc;
-  float e = dq[(int64_t)row * lddq + col], o = dq[(int64_t)row * lddq + col + 1];
-  if (rope) {
-    const float2 cs = rope[(int64_t)row * (D / 2) + (col % D) / 2];
-    const float e2 = e * cs.x + o * cs.y;
-    const float o2 = -e * cs.y + o * cs.x;
-    e = e2;
-    o = o2;
-  }
-  out[(int64_t)row * ldo + col] = from_f32<T>(e);
-  out[(int64_t)row * ldo + col + 1] = from_f32<T>(o);
 }
 
 }  // namespace bpt
