@@ -69,11 +69,13 @@ class BptError(RuntimeError):
 _LIB: Optional[ctypes.CDLL] = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libbpt.so (once). Raises if it has not been built."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libbpt.so (once; BPT_LIBRARY overrides the path). Raises if it has
+    not been built."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    path = path or os.environ.get("BPT_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} not found: build it with `python -m memory_efficient_long_amd.build`")
     lib = ctypes.CDLL(path)

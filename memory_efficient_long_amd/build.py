@@ -36,17 +36,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libbpt.so)")
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "bpt_layer.hip")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(REPO, "include"), src, "-o", tmp]
+def build(verbose: bool = False, out: str = LIB_PATH, csrc: str = CSRC, defines=()) -> str:
+    src = os.path.join(csrc, "bpt_layer.hip")
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(REPO, "include"),
+           src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-6000:]}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

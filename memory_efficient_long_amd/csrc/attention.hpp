@@ -29,6 +29,8 @@
 // factor are applied when dQ and dK are written.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace bpt {
@@ -72,6 +74,24 @@ __device__ __forceinline__ void map_head_tile(int bid, int nheads, int ntiles, b
   tile = reverse ? ntiles - 1 - j : j;
 }
 
+// Row-major LDS tile of R x D elements, rows padded by 16 bytes and stored at
+// permuted positions pi(r) = r ^ ((r >> 3) & 7). With the pad, eight
+// consecutive rows (one MFMA fragment read) start on distinct banks; the
+// permutation also spreads rows 4 apart (the RowTile store pattern) over
+// distinct banks. The permutation is per row, so a lane's base address is
+// computed once and fragment offsets stay immediates.
+template <typename T, int D>
+struct Swz {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int LD = D + VEC;
+  __device__ static __forceinline__ int row(int r) { return r ^ ((r >> 3) & 7); }
+  __device__ static __forceinline__ int off(int r, int chunk) { return row(r) * LD + chunk * VEC; }
+  // Fragment: 8 consecutive elements [k0, k0 + 8) of row r (k0 % 8 == 0).
+  __device__ static __forceinline__ typename Frag<T>::type frag(const T* tile, int r, int k0) {
+    return ld_frag(tile + row(r) * LD + k0);
+  }
+};
+
 // A tile of R rows x D columns (storage T, row stride ld) held in registers as
 // 4-row x 16-byte sub-blocks, stored to LDS row-major and/or transposed.
 // Consecutive threads take consecutive 4-row groups, so the transposed store
@@ -96,14 +116,14 @@ struct RowTile {
       }
     }
   }
-  __device__ __forceinline__ void store_rows(T* lds, int ldl, int tid) const {
+  __device__ __forceinline__ void store_swz(T* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int sb = tid + 256 * i;
       if (sb < SB) {
         const int rb = sb % (R / 4), cb = sb / (R / 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st<u32x4>(lds + (4 * rb + j) * ldl + cb * VEC, reg[i][j]);
+        for (int j = 0; j < 4; ++j) st<u32x4>(lds + Swz<T, D>::off(4 * rb + j, cb), reg[i][j]);
       }
     }
   }
@@ -135,20 +155,17 @@ __device__ __forceinline__ typename Frag<T>::type zero_frag() {
   return pack_frag<T>(z);
 }
 
-// Row pitches (elements) of the LDS tiles: +16 bytes for rows read as 16-byte
-// fragments, +8 (bf16) / +16 (fp32) bytes for transposed tiles read as two
-// 4-element halves.
-template <typename T> constexpr int pad_row() { return 16 / (int)sizeof(T); }
+// Row pitch padding (elements) of the transposed LDS tiles, read as two
+// 4-element halves: 8 bytes (bf16) / 16 bytes (fp32).
 template <typename T> constexpr int pad_t() { return sizeof(T) == 2 ? 4 : 4; }
 
 // ============================================================================ forward
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   constexpr int BQ = 128, BKV = 64;
-  constexpr int LDK = D + pad_row<T>();
   constexpr int LDV = BKV + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) T ks[2][BKV * LDK];
+  __shared__ __attribute__((aligned(16))) T ks[2][BKV * (D + 16 / sizeof(T))];
   __shared__ __attribute__((aligned(16))) T vt[2][D * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -185,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   if (ntiles > 0) {
     kt.load(Kp, D, 0, s, tid);
     vtile.load(Vp, D, 0, s, tid);
-    kt.store_rows(ks[0], LDK, tid);
+    kt.store_swz(ks[0], tid);
     vtile.store_cols(vt[0], LDV, tid);
   }
   __syncthreads();
@@ -197,18 +214,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       vtile.load(Vp, D, (t + 1) * BKV, s, tid);
     }
     if (wave_active && t < wave_tiles) {
+      const int kvb = t * BKV;
+      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          auto kf = ld_frag(&ks[buf][(32 * sb + lr) * LDK + 16 * c + 8 * g]);
+          auto kf = Swz<T, D>::frag(ks[buf], 32 * sb + lr, 16 * c + 8 * g);
           sacc[sb] = mma(kf, qf[c], sacc[sb]);
         }
       }
-      const int kvb = t * BKV;
-      const bool need_mask = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
-      if (need_mask) {  // wave-uniform; keys past min(query, s - 1) get -inf
+      if (MASK) {  // wave-uniform; keys past min(query, s - 1) get -inf
         const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       }
     }
     if (t + 1 < ntiles) {
-      kt.store_rows(ks[buf ^ 1], LDK, tid);
+      kt.store_swz(ks[buf ^ 1], tid);
       vtile.store_cols(vt[buf ^ 1], LDV, tid);
     }
     __syncthreads();
@@ -283,15 +300,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
   constexpr int BQ = 64, BKV = 128;
-  constexpr int LDR = D + pad_row<T>();
   constexpr int LDT = BQ + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) T qs[BQ * LDR];
-  __shared__ __attribute__((aligned(16))) T dos[BQ * LDR];
-  __shared__ __attribute__((aligned(16))) T qts[D * LDT];
-  __shared__ __attribute__((aligned(16))) T dots[D * LDT];
-  __shared__ __attribute__((aligned(16))) float lse_s[BQ];
-  __shared__ __attribute__((aligned(16))) float dd_s[BQ];
+  // Two LDS stages: the next query tile is stored while this one is consumed.
+  __shared__ __attribute__((aligned(16))) T qs[2][BQ * Swz<T, D>::LD];
+  __shared__ __attribute__((aligned(16))) T dos[2][BQ * Swz<T, D>::LD];
+  __shared__ __attribute__((aligned(16))) T qts[2][D * LDT];
+  __shared__ __attribute__((aligned(16))) T dots[2][D * LDT];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dd_s[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, g = lane >> 5;
@@ -335,34 +352,47 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
       dd_r = qr < s ? a.dvec[(int64_t)hq * s + qr] : 0.f;
     }
   };
-  if (nsteps > 0) load_step(0);
+  auto store_step = [&](int buf) {
+    qtile.store_swz(qs[buf], tid);
+    qtile.store_cols(qts[buf], LDT, tid);
+    dotile.store_swz(dos[buf], tid);
+    dotile.store_cols(dots[buf], LDT, tid);
+    if (tid < BQ) { lse_s[buf][tid] = lse_r; dd_s[buf][tid] = dd_r; }
+  };
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
 
   for (int step = 0; step < nsteps; ++step) {
     const int q0 = (qt0 + step % per_head) * BQ;
-    __syncthreads();
-    qtile.store_rows(qs, LDR, tid);
-    qtile.store_cols(qts, LDT, tid);
-    dotile.store_rows(dos, LDR, tid);
-    dotile.store_cols(dots, LDT, tid);
-    if (tid < BQ) { lse_s[tid] = lse_r; dd_s[tid] = dd_r; }
-    __syncthreads();
+    const int buf = step & 1;
     if (step + 1 < nsteps) load_step(step + 1);
+    const T* qsb = qs[buf];
+    const T* dosb = dos[buf];
+    const T* qtsb = qts[buf];
+    const T* dotsb = dots[buf];
+    const float* lseb = lse_s[buf];
+    const float* ddb = dd_s[buf];
 
+    // Steps touching the diagonal (or the sequence end) need the mask.
+    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S = Q K^T and dP = dO V^T for this wave's 32 keys (lane = key).
       f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc = mma(ld_frag(&qs[(32 * qb + lr) * LDR + 16 * c + 8 * g]), kf[c], sacc);
-        dpacc = mma(ld_frag(&dos[(32 * qb + lr) * LDR + 16 * c + 8 * g]), vf[c], dpacc);
+        sacc = mma(Swz<T, D>::frag(qsb, 32 * qb + lr, 16 * c + 8 * g), kf[c], sacc);
+        dpacc = mma(Swz<T, D>::frag(dosb, 32 * qb + lr, 16 * c + 8 * g), vf[c], dpacc);
       }
       // Row terms of rows acc_row(4k..4k+3) are 4 consecutive floats.
       f32x4 l4[4], d4[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        l4[k] = ld<f32x4>(&lse_s[32 * qb + 8 * k + 4 * g]);
-        d4[k] = ld<f32x4>(&dd_s[32 * qb + 8 * k + 4 * g]);
+        l4[k] = ld<f32x4>(&lseb[32 * qb + 8 * k + 4 * g]);
+        d4[k] = ld<f32x4>(&ddb[32 * qb + 8 * k + 4 * g]);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -370,8 +400,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
         sacc[r] = p;
         dpacc[r] = p * (dpacc[r] - d4[r >> 2][r & 3]);
       }
-      // Causal / tail mask (wave-uniform test): key row must be <= min(query, s - 1).
-      if ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s) {
+      // Causal / tail mask: key row must be <= min(query, s - 1).
+      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qg = q0 + 32 * qb + acc_row(r, g);
@@ -394,13 +424,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
         const auto dsa = pack_frag<T>(td);
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
-          const T* dor = &dots[(32 * i + lr) * LDT + 16 * cc + 4 * g];
+          const T* dor = &dotsb[(32 * i + lr) * LDT + 16 * cc + 4 * g];
           dvacc[i] = mma(pa, ld_frag_split(dor, dor + 8), dvacc[i]);
-          const T* qr = &qts[(32 * i + lr) * LDT + 16 * cc + 4 * g];
+          const T* qr = &qtsb[(32 * i + lr) * LDT + 16 * cc + 4 * g];
           dkacc[i] = mma(dsa, ld_frag_split(qr, qr + 8), dkacc[i]);
         }
       }
     }
+    if (step + 1 < nsteps) store_step(buf ^ 1);
+    __syncthreads();
   }
 
   // dK (scaled, inverse RoPE) and dV to the token-major outputs.
@@ -428,11 +460,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   constexpr int BQ = 128, BKV = 64;
-  constexpr int LDR = D + pad_row<T>();
   constexpr int LDT = BKV + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
-  __shared__ __attribute__((aligned(16))) T ks[BKV * LDR];
-  __shared__ __attribute__((aligned(16))) T vs[BKV * LDR];
+  __shared__ __attribute__((aligned(16))) T ks[BKV * Swz<T, D>::LD];
+  __shared__ __attribute__((aligned(16))) T vs[BKV * Swz<T, D>::LD];
   __shared__ __attribute__((aligned(16))) T kts[D * LDT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -477,9 +508,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   }
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
-    ktile.store_rows(ks, LDR, tid);
+    ktile.store_swz(ks, tid);
     ktile.store_cols(kts, LDT, tid);
-    vtile.store_rows(vs, LDR, tid);
+    vtile.store_swz(vs, tid);
     __syncthreads();
     if (t + 1 < ntiles) {
       ktile.load(Kp, D, (t + 1) * BKV, s, tid);
@@ -487,22 +518,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
     }
     if (wave_active && t < wave_tiles) {
       const int kvb = t * BKV;
-      const bool need_mask = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         // S^T = K Q^T and dP^T = V dO^T (lane = query row).
         f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          sacc = mma(ld_frag(&ks[(32 * sb + lr) * LDR + 16 * c + 8 * g]), qf[c], sacc);
-          dpacc = mma(ld_frag(&vs[(32 * sb + lr) * LDR + 16 * c + 8 * g]), df[c], dpacc);
+          sacc = mma(Swz<T, D>::frag(ks, 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc);
+          dpacc = mma(Swz<T, D>::frag(vs, 32 * sb + lr, 16 * c + 8 * g), df[c], dpacc);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
           dpacc[r] = p * (dpacc[r] - dd_q);
         }
-        if (need_mask) {  // wave-uniform; keys past min(query, s - 1) contribute nothing
+        if (MASK) {  // wave-uniform; keys past min(query, s - 1) contribute nothing
           const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb - 32 * sb;
 #pragma unroll
           for (int r = 0; r < 16; ++r) dpacc[r] = (acc_row(r, g) > lim) ? 0.f : dpacc[r];
