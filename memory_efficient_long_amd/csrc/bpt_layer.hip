@@ -235,11 +235,23 @@ size_t saved_bytes(const Plan& p) {
 }
 
 // ----------------------------------------------------------------- launchers
+template <typename T, bool AK, bool BK, int BM, int BN, int BKK, int WM, int WN, class Epi>
+void launch_gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
+                 int64_t N, int64_t K, const Epi& epi, bool even) {
+  const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (even)
+    hipLaunchKernelGGL((gemm_kernel<T, AK, BK, BM, BN, BKK, WM, WN, true, Epi>), dim3((unsigned)nt),
+                       dim3(256), 0, st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, AK, BK, BM, BN, BKK, WM, WN, false, Epi>), dim3((unsigned)nt),
+                       dim3(256), 0, st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+}
+
 template <typename T, bool AK, bool BK, class Epi>
 bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
                 int64_t N, int64_t K, const Epi& epi, const char* what) {
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int BM = 128, BN = 128, BKK = sizeof(T) == 2 ? 64 : 32;
+  constexpr int BKK = sizeof(T) == 2 ? 64 : 32;
   // Layout invariants of the tile loaders (16-byte vectors along the
   // contiguous axis, every vector fully inside or outside the matrix).
   bool ok = M >= 0 && N >= 0 && K >= 0 && M < (1LL << 31) && N < (1LL << 31) && K < (1LL << 31);
@@ -248,11 +260,12 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
   ok = ok && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % VEC == 0) &&
        (ldb % VEC == 0);
   if (!ok) return fail(BPT_EUNSUPPORTED, std::string("gemm layout invariant: ") + what);
-  const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (nt == 0) return BPT_OK;
+  if (M == 0 || N == 0) return BPT_OK;
   TimedLaunch tl(BPT_KERNEL_GEMM, st);
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BK, BM, BN, BKK, Epi>), dim3((unsigned)nt), dim3(256), 0,
-                     st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+  // 128 x 128 tiles, 4 waves of 64 x 64: two workgroups per CU (8 waves) hide
+  // latency better than larger single-workgroup tiles on the measured shapes.
+  const bool even = M % 128 == 0 && N % 128 == 0 && K % BKK == 0;
+  launch_gemm<T, AK, BK, 128, 128, BKK, 64, 64>(st, A, lda, B, ldb, M, N, K, epi, even);
   return check_launch(what);
 }
 

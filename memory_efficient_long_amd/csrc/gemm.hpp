@@ -14,9 +14,10 @@
 // layout the layer needs (forward x W, backward dY W^T and X^T dY) runs on the
 // same MFMA inner loop without separate transpose passes.
 //
-// Workgroup: 256 threads = 2 x 2 waves; each wave owns a (BM/2) x (BN/2)
-// block of 32x32 MFMA tiles. Global loads of the next K step are issued before
-// the current step's MFMAs (register prefetch, LDS double buffer).
+// Workgroup: 256 threads = 4 waves, each owning a (BM/2) x (BN/2) block of
+// 32 x 32 MFMA tiles (the layer uses 128 x 128 tiles: two workgroups per CU). Global loads of
+// the next K step are issued before the current step's MFMAs (register
+// prefetch, LDS double buffer).
 #pragma once
 
 #include "device_common.hpp"
@@ -141,37 +142,43 @@ struct EpiSwiGrad {
 
 // ----------------------------------------------------------------- tile loaders
 // Loads one operand tile (R rows x BK reduction) into registers and stores it
-// K-contiguous into LDS. Per thread: 4 vector loads of 16 bytes.
-template <typename T, bool KMAJ, int R, int BK>
+// K-contiguous into LDS (rows padded by 16 bytes). K-major sources are read as
+// 16-byte row chunks; MN-major sources as 4(k) x 16-byte sub-blocks that are
+// transposed in registers. EVEN skips the bounds checks (every tile is full).
+template <typename T, bool KMAJ, int R, int BK, bool EVEN>
 struct TileLoader {
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int LDK = BK + VEC;
-  static constexpr int N_LOADS = 4;
-  static_assert(R * BK / VEC == 4 * 256, "tile must be 4 x 16 B per thread");
-  u32x4 reg[4];
+  static constexpr int CHUNKS = R * BK / VEC;            // 16-byte chunks per tile
+  static constexpr int PER = CHUNKS / 256;               // per thread
+  static_assert(CHUNKS % 1024 == 0, "tile must be a multiple of 4 x 16 B per thread");
+  u32x4 reg[PER];
 
-  // rows [row0, row0 + R) of limit rlim; reduction [k0, k0 + BK) of limit K
   __device__ __forceinline__ void load(const T* __restrict__ src, int64_t ldm, int row0, int rlim,
                                        int k0, int K, int tid) {
     if constexpr (KMAJ) {
       constexpr int CPR = BK / VEC;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PER; ++i) {
         const int c = tid + 256 * i;
         const int r = c / CPR, kc = (c % CPR) * VEC;
         const int gr = row0 + r, gk = k0 + kc;
-        if (gr < rlim && gk < K) reg[i] = ld<u32x4>(src + (int64_t)gr * ldm + gk);
+        if (EVEN || (gr < rlim && gk < K)) reg[i] = ld<u32x4>(src + (int64_t)gr * ldm + gk);
         else reg[i] = u32x4{0u, 0u, 0u, 0u};
       }
     } else {
       constexpr int KB = BK / 4;
-      const int kb = tid % KB, rb = tid / KB;
-      const int gr = row0 + rb * VEC;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gk = k0 + 4 * kb + i;
-        if (gr < rlim && gk < K) reg[i] = ld<u32x4>(src + (int64_t)gk * ldm + gr);
-        else reg[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < PER / 4; ++i) {
+        const int sb = tid + 256 * i;
+        const int kb = sb % KB, rb = sb / KB;
+        const int gr = row0 + rb * VEC;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int gk = k0 + 4 * kb + j;
+          if (EVEN || (gr < rlim && gk < K)) reg[4 * i + j] = ld<u32x4>(src + (int64_t)gk * ldm + gr);
+          else reg[4 * i + j] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   }
@@ -180,37 +187,45 @@ struct TileLoader {
     if constexpr (KMAJ) {
       constexpr int CPR = BK / VEC;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < PER; ++i) {
         const int c = tid + 256 * i;
         const int r = c / CPR, kc = (c % CPR) * VEC;
         st<u32x4>(tile + r * LDK + kc, reg[i]);
       }
     } else {
       constexpr int KB = BK / 4;
-      const int kb = tid % KB, rb = tid / KB;
-      if constexpr (sizeof(T) == 2) {
-        u32x2 out[8];
-        transpose_4xvec(reg, out);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st<u32x2>(tile + (rb * 8 + j) * LDK + 4 * kb, out[j]);
-      } else {
-        u32x4 out[4];
-        transpose_4xvec(reg, out);
+      for (int i = 0; i < PER / 4; ++i) {
+        const int sb = tid + 256 * i;
+        const int kb = sb % KB, rb = sb / KB;
+        if constexpr (sizeof(T) == 2) {
+          u32x2 out[8];
+          transpose_4xvec(&reg[4 * i], out);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st<u32x4>(tile + (rb * 4 + j) * LDK + 4 * kb, out[j]);
+          for (int j = 0; j < 8; ++j) st<u32x2>(tile + (rb * 8 + j) * LDK + 4 * kb, out[j]);
+        } else {
+          u32x4 out[4];
+          transpose_4xvec(&reg[4 * i], out);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st<u32x4>(tile + (rb * 4 + j) * LDK + 4 * kb, out[j]);
+        }
       }
     }
   }
 };
 
 // ----------------------------------------------------------------- kernel
-template <typename T, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, class Epi>
+// BM x BN output tile per workgroup of 4 waves arranged (BM/WM) x (BN/WN);
+// each wave owns WM x WN as (WM/32) x (WN/32) MFMA tiles.
+template <typename T, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int WM, int WN, bool EVEN,
+          class Epi>
 __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int64_t lda,
                                                    const T* __restrict__ B, int64_t ldb, int M,
                                                    int N, int K, Epi epi) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LDK = BK + VEC;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WGN = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == 4, "4 waves per workgroup");
   constexpr int FM = WM / 32, FN = WN / 32;
   __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LDK];
 
@@ -236,10 +251,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
   const int tm = first_m + (tile % (GROUP * tiles_n)) % gsz;
   const int tn = (tile % (GROUP * tiles_n)) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * WN;
+  const int wm0 = (w / WGN) * WM, wn0 = (w % WGN) * WN;
 
-  TileLoader<T, A_KMAJ, BM, BK> la;
-  TileLoader<T, B_KMAJ, BN, BK> lb;
+  TileLoader<T, A_KMAJ, BM, BK, EVEN> la;
+  TileLoader<T, B_KMAJ, BN, BK, EVEN> lb;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -294,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
         float v = acc[i][j][r];
         float vp = 0.f;
         if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
-        if (row < M && col < N) epi(row, col, v, vp);
+        if (EVEN || (row < M && col < N)) epi(row, col, v, vp);
       }
     }
 }
