@@ -16,7 +16,6 @@ bounded sample (``cpu_baseline``).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,18 +41,15 @@ def model_flops(sh) -> dict:
     lin = 2 * s * h * (H + 2 * Hkv) * d + 2 * s * H * d * h + 2 * s * h * f * n_ffn
     attn = 4 * d * H * attn_pairs(s, sh.causal)
     fwd = (lin + attn) * sh.batch
-    return {"fwd": fwd, "step": 3 * fwd, "attn_fwd": 4 * d * H * attn_pairs(s, sh.causal) * sh.batch,
-            "attn_bwd": 8 * d * H * attn_pairs(s, sh.causal) * sh.batch}
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "memory_efficient_long_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode())
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    pairs = attn_pairs(s, sh.causal) * sh.batch
+    # Algorithmic attention FLOPs per kernel: forward QK^T and PV (4d per
+    # visible pair and head); backward dV, dP, dK in the dK/dV pass (6d) and dQ
+    # in the dQ pass (2d). "hw_" adds the recomputed products each kernel runs.
+    return {"fwd": fwd, "step": 3 * fwd,
+            "attn_fwd": 4 * d * H * pairs, "attn_bwd_dkdv": 6 * d * H * pairs,
+            "attn_bwd_dq": 2 * d * H * pairs,
+            "hw_attn_fwd": 4 * d * H * pairs, "hw_attn_bwd_dkdv": 8 * d * H * pairs,
+            "hw_attn_bwd_dq": 6 * d * H * pairs}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -64,6 +60,7 @@ def load_traffic(kernel: str, workload: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
+    from memory_efficient_long_amd.profiling import kernel_source_hash
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -107,7 +104,20 @@ def main() -> int:
     ap.add_argument("--cpu-sample-len", type=int, default=2048)
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -164,7 +174,8 @@ def main() -> int:
         bwd()
     torch.cuda.synchronize()
 
-    classes = ["attn_fwd", "attn_bwd"] + (["gemm", "rowwise"] if args.breakdown else [])
+    attn_classes = ["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"]
+    classes = attn_classes + (["gemm", "rowwise"] if args.breakdown else [])
     bpt.bpt_timing_enable(classes)
     bpt.bpt_timing_read(reset=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -193,18 +204,19 @@ def main() -> int:
     tflops = fl["step"] / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
 
-    # Dominant kernel: the attention class with the larger measured time.
-    dom = max(("attn_fwd", "attn_bwd"), key=lambda c: timing[c][0])
+    # Dominant kernel: the attention kernel with the largest measured time.
+    dom = max(attn_classes, key=lambda c: timing[c][0])
     dom_ms, dom_n = timing[dom]
     avg_ms = dom_ms / max(dom_n, 1)
     per_launch_flops = fl[dom] / max(dom_n / args.steps, 1)
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
-    kernel_name = {"attn_fwd": "attn_fwd_kernel", "attn_bwd": "attn_bwd_kernel"}[dom]
+    kernel_name = dom + "_kernel"
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": load_traffic(kernel_name, sh.name), "kernel": kernel_name,
                 "avg_launch_ms": round(avg_ms, 3), "launches_per_step": dom_n / args.steps,
-                "algorithmic_flops_per_launch": per_launch_flops}
+                "algorithmic_flops_per_launch": per_launch_flops,
+                "hardware_flops_per_launch": fl["hw_" + dom] / max(dom_n / args.steps, 1)}
 
     breakdown = {c: {"ms_per_step": round(v[0] / args.steps, 3), "launches_per_step": v[1] / args.steps}
                  for c, v in timing.items() if v[1]}

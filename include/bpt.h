@@ -146,11 +146,12 @@ const char* bpt_status_string(bpt_status status);
  * is process-wide (shared by all threads and devices); calls that overlap
  * while timing is enabled are attributed to whichever class they launch. */
 typedef enum {
-  BPT_KERNEL_ATTN_FWD = 0, /* blockwise attention forward                      */
-  BPT_KERNEL_ATTN_BWD = 1, /* attention backward (dK, dV, dQ accumulation)     */
-  BPT_KERNEL_GEMM = 2,     /* projections and FFN GEMMs with fused epilogues   */
-  BPT_KERNEL_ROWWISE = 3,  /* norms, reductions, RoPE table, fills, dQ/D passes */
-  BPT_KERNEL_CLASSES = 4
+  BPT_KERNEL_ATTN_FWD = 0,     /* blockwise attention forward                     */
+  BPT_KERNEL_ATTN_BWD_DKDV = 1, /* attention backward, dK and dV pass             */
+  BPT_KERNEL_ATTN_BWD_DQ = 2,  /* attention backward, dQ pass                     */
+  BPT_KERNEL_GEMM = 3,         /* projections and FFN GEMMs with fused epilogues  */
+  BPT_KERNEL_ROWWISE = 4,      /* norms, reductions, RoPE table, fills, D = rowsum */
+  BPT_KERNEL_CLASSES = 5
 } bpt_kernel_class;
 
 /* Enable timing for the classes whose bit (1 << class) is set; 0 disables. */

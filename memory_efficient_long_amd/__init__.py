@@ -175,7 +175,7 @@ def bpt_last_error() -> str:
     return load_library().bpt_last_error().decode()
 
 
-KERNEL_CLASSES = ["attn_fwd", "attn_bwd", "gemm", "rowwise"]
+KERNEL_CLASSES = ["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm", "rowwise"]
 
 
 def bpt_timing_enable(classes) -> int:

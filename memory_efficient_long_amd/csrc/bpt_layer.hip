@@ -61,8 +61,8 @@ struct TimingState {
   struct Rec { int cls; hipEvent_t a, b; };
   std::vector<Rec> pending;
   std::vector<hipEvent_t> pool;
-  double ms[BPT_KERNEL_CLASSES] = {0, 0, 0, 0};
-  int64_t n[BPT_KERNEL_CLASSES] = {0, 0, 0, 0};
+  double ms[BPT_KERNEL_CLASSES] = {};
+  int64_t n[BPT_KERNEL_CLASSES] = {};
 };
 TimingState& timing() {
   static TimingState t;
@@ -370,23 +370,22 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.scale = (float)(1.0 / std::sqrt((double)p.D));
   const dim3 gkv((unsigned)(p.nkvc * ((p.s + 127) / 128))), gq((unsigned)(p.U * ((p.s + 127) / 128)));
   const dim3 blk(256);
-  TimedLaunch tl(BPT_KERNEL_ATTN_BWD, st);
-  if constexpr (sizeof(T) == 2) {
-    if (p.D == 128) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 128>), gkv, blk, 0, st, a);
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 128>), gq, blk, 0, st, a);
-      return check_launch("attn_bwd");
-    }
+  if (p.D == 128 && sizeof(T) != 2)
+    return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
+  {
+    TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DKDV, st);
+    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, sizeof(T) == 2 ? 128 : 64>), gkv, blk, 0, st, a);
+    else if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
   }
-  if (p.D == 128) return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
-  if (p.D == 64) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
+  BPT_TRY(check_launch("attn_bwd_dkdv"));
+  {
+    TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DQ, st);
+    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, sizeof(T) == 2 ? 128 : 64>), gq, blk, 0, st, a);
+    else if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
   }
-  return check_launch("attn_bwd");
+  return check_launch("attn_bwd_dq");
 }
 
 // Q, K, V of head chunk c (query heads [c U, (c+1) U)) into head-major buffers.

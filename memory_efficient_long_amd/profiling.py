@@ -1,0 +1,120 @@
+"""Turn rocprofv3 output into the short summaries kept under ``profiles/``.
+
+    python -m memory_efficient_long_amd.profiling stats RUN_kernel_stats.csv \
+        --out profiles/NAME.md --cmd "the command that produced it"
+    python -m memory_efficient_long_amd.profiling traffic --kernel attn_bwd_dkdv_kernel \
+        --workload gpt1b-s128k --fetch F.csv --write W.csv --calib-fetch CF.csv \
+        --calib-write CW.csv --copy-bytes N --out profiles/KERNEL_WORKLOAD_traffic.json
+
+``traffic`` scales the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of
+the kernel by what the same counters read for a device copy of a known number
+of bytes (the calibration run of ``bench.py --calibrate-copy``), and records
+the hash of the kernel sources so a later kernel change invalidates it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG_DIR, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = re.sub(r"^void ", "", name)
+    m = re.match(r"_ZN3bpt\d+(\w+?)I", name)
+    base = m.group(1) if m else re.sub(r"[<(].*", "", name)
+    return base
+
+
+def cmd_stats(args) -> None:
+    rows = list(csv.DictReader(open(args.csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# rocprofv3 kernel statistics: {args.title}", "",
+             f"Command: `{args.cmd}`", "",
+             "| kernel | calls | total ms | avg ms | % |", "|---|---|---|---|---|"]
+    for r in rows[: args.top]:
+        tot = float(r["TotalDurationNs"]) / 1e6
+        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {tot:.3f} | "
+                     f"{float(r['AverageNs']) / 1e6:.4f} | {100 * float(r['TotalDurationNs']) / total:.1f} |")
+    lines += ["", f"Total kernel time: {total / 1e6:.3f} ms over all listed dispatches."]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path: str, counter: str, kernel_sub: str):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        if kernel_sub not in r["Kernel_Name"]:
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def cmd_traffic(args) -> None:
+    fetch = _per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    write = _per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    cf = _per_dispatch(args.calib_fetch, "FETCH_SIZE", args.calib_kernel)
+    cw = _per_dispatch(args.calib_write, "WRITE_SIZE", args.calib_kernel)
+    if not (fetch and write and cf and cw):
+        sys.exit("missing counter rows")
+    kib_fetch_copy = statistics.median(cf)
+    kib_write_copy = statistics.median(cw)
+    f_scale = args.copy_bytes / kib_fetch_copy
+    w_scale = args.copy_bytes / kib_write_copy
+    rec = {
+        "kernel": args.kernel, "workload": args.workload,
+        "fetch_kib_per_dispatch": statistics.median(fetch),
+        "write_kib_per_dispatch": statistics.median(write),
+        "copy_bytes": args.copy_bytes,
+        "copy_fetch_kib": kib_fetch_copy, "copy_write_kib": kib_write_copy,
+        "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
+        "hbm_bytes_per_launch": statistics.median(fetch) * f_scale + statistics.median(write) * w_scale,
+        "kernel_source_hash": kernel_source_hash(),
+        "command": args.cmd,
+    }
+    with open(args.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--out", required=True)
+    s.add_argument("--cmd", default="")
+    s.add_argument("--title", default="")
+    s.add_argument("--top", type=int, default=25)
+    t = sub.add_parser("traffic")
+    for k in ("kernel", "workload", "fetch", "write", "calib_fetch", "calib_write", "out"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--calib-kernel", default="copy")
+    t.add_argument("--cmd", default="")
+    args = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic}[args.cmd_name](args)
+
+
+if __name__ == "__main__":
+    main()
