@@ -1,0 +1,467 @@
+// bf16 attention kernels (head_dim 64 / 128) whose key/value and query tiles
+// travel global -> LDS by direct LDS loads (global_load_lds_dwordx4: lane l's
+// 16 bytes land at the instruction's LDS base + 16 l), so no register staging
+// and no in-register transposes are needed. Tiles are row-major, unpadded,
+// with the 16-byte chunks of row r XOR-permuted by f(r) = 2 (r & 3) +
+// ((r >> 2) & 1): eight consecutive rows (a row-operand fragment read) and
+// four consecutive rows (a transpose read) fall on distinct banks. Operands
+// that need the transposed tile (V^T in the forward, dO^T and Q^T in the
+// dK/dV pass, K^T in the dQ pass) are read with ds_read_b64_tr_b16, which,
+// within each 16-lane group, gives lane i element (i % 4) of the 8-byte piece
+// addressed by lane 4e + i / 4 as its element e: one read yields four
+// consecutive rows of one column per lane.
+//
+// The computation is the one documented in attention.hpp (same tiling, same
+// lane-local softmax statistics, same permuted reduction order); only the
+// staging differs. Register use drops enough for two waves per SIMD in all
+// three kernels.
+#pragma once
+
+#include "attention.hpp"
+
+namespace bpt {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct DmaTile {
+  static constexpr int RB = D * 2;   // row bytes (bf16)
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static_assert(CPR >= 8, "head_dim must be >= 64");
+  __device__ static __forceinline__ int f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+  __device__ static __forceinline__ int off(int r, int chunk) {
+    return r * RB + ((chunk ^ f(r)) << 4);
+  }
+
+  // Issue the direct loads of rows [row0, row0 + R) of src (row stride ld
+  // elements) into tile; rows at or past rlim repeat row rlim - 1 (they are
+  // masked by the caller). NW waves share the tile.
+  template <int R, int NW>
+  __device__ static __forceinline__ void load(bf16* tile, const bf16* src, int64_t ld, int row0,
+                                              int rlim, int w, int lane) {
+    constexpr int PERW = R * RB / 1024 / NW;
+    static_assert(PERW >= 1 && R * RB % (1024 * NW) == 0, "tile split");
+#pragma unroll
+    for (int m = 0; m < PERW; ++m) {
+      const int base = (w * PERW + m) * 1024;
+      const int o = base + 16 * lane;
+      const int r = o / RB, p = (o % RB) >> 4;
+      const int gr = min(row0 + r, rlim - 1);
+      const bf16* gp = src + (int64_t)gr * ld + ((p ^ f(r)) << 3);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)gp,
+          (__attribute__((address_space(3))) void*)((char*)tile + base), 16, 0, 0);
+    }
+  }
+
+  // Elements [k0, k0 + 8) of row r (k0 % 8 == 0).
+  __device__ static __forceinline__ bf16x8 frag(const bf16* tile, int r, int k0) {
+    return ld<bf16x8>((const char*)tile + off(r, k0 >> 3));
+  }
+
+  // Transposed-operand fragment for output column n = 32 i + (lane % 32) and
+  // reduction chunk cc: elements 0-3 = rows 16cc + 4g + {0..3}, elements 4-7 =
+  // rows 16cc + 8 + 4g + {0..3} (g = lane / 32), all at column n.
+  __device__ static __forceinline__ bf16x8 tr_frag(const bf16* tile, int cc, int i, int lane) {
+    const int li = lane & 15, g = lane >> 5;
+    const int col = 32 * i + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+    const int r0 = 16 * cc + 4 * g + (li >> 2);
+    const int pc = ((col >> 3) ^ f(r0)) << 4;  // f(r0 + 8) == f(r0)
+    const int pb = ((col >> 2) & 1) << 3;
+    const char* b0 = (const char*)tile + r0 * RB + pc + pb;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)b0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(b0 + 8 * RB));
+    u32x4 v;
+    v[0] = (unsigned)(unsigned short)lo[0] | ((unsigned)(unsigned short)lo[1] << 16);
+    v[1] = (unsigned)(unsigned short)lo[2] | ((unsigned)(unsigned short)lo[3] << 16);
+    v[2] = (unsigned)(unsigned short)hi[0] | ((unsigned)(unsigned short)hi[1] << 16);
+    v[3] = (unsigned)(unsigned short)hi[2] | ((unsigned)(unsigned short)hi[3] << 16);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ============================================================================ forward
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> a) {
+  using TL = DmaTile<D>;
+  constexpr int BQ = 128, BKV = 64;
+  constexpr int NC = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 ks[2][BKV * D];
+  __shared__ __attribute__((aligned(1024))) bf16 vs[2][BKV * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, g = lane >> 5;
+  const int s = a.s;
+  const int nqt = (s + BQ - 1) / BQ;
+  int hq, qt;
+  map_head_tile(blockIdx.x, a.nh, nqt, a.causal != 0, hq, qt);
+  const int hk = hq / a.group;
+  const int q0 = qt * BQ;
+  const int qrow = q0 + 32 * w + lr;
+  const bf16* Qp = a.q + (int64_t)hq * s * D;
+  const bf16* Kp = a.k + (int64_t)hk * s * D;
+  const bf16* Vp = a.v + (int64_t)hk * s * D;
+
+  bf16x8 qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qf[c] = qrow < s ? ld_frag(Qp + (int64_t)qrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
+
+  const int kv_end = a.causal ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const bool wave_active = q0 + 32 * w < s;
+  const int wave_last = min(q0 + 32 * w + 31, s - 1);
+  const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+
+  f32x16 oacc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) oacc[i] = zero16();
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  if (ntiles > 0) {
+    TL::template load<BKV, 4>(ks[0], Kp, D, 0, s, w, lane);
+    TL::template load<BKV, 4>(vs[0], Vp, D, 0, s, w, lane);
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      TL::template load<BKV, 4>(ks[buf ^ 1], Kp, D, (t + 1) * BKV, s, w, lane);
+      TL::template load<BKV, 4>(vs[buf ^ 1], Vp, D, (t + 1) * BKV, s, w, lane);
+    }
+    if (wave_active && t < wave_tiles) {
+      const int kvb = t * BKV;
+      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      f32x16 sacc[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+          sacc[sb] = mma(TL::frag(ks[buf], 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc[sb]);
+      if (MASK) {  // wave-uniform; keys past min(query, s - 1) get -inf
+        const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[sb][r] = (32 * sb + acc_row(r, g) > lim) ? -INFINITY : sacc[sb][r];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        m_run = m_new;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[sb][r], sl2, -m_run));
+          sacc[sb][r] = p;
+          rs += p;
+        }
+      l_run += rs + shfl_xor(rs, 32);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        float tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = sacc[cc >> 1][8 * (cc & 1) + e];
+        const bf16x8 pf = pack_frag<bf16>(tmp);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) oacc[i] = mma(TL::tr_frag(vs[buf], cc, i, lane), pf, oacc[i]);
+      }
+    }
+    wait_dma();
+    __syncthreads();
+  }
+
+  if (wave_active && qrow < s) {
+    const float inv_l = 1.f / l_run;
+    bf16* orow = a.o + (int64_t)qrow * a.ldo + (int64_t)hq * D;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * i + r4 * 8 + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) orow[d + e] = (bf16)(oacc[i][4 * r4 + e] * inv_l);
+      }
+    if (g == 0) a.lse[(int64_t)hq * s + qrow] = m_run + __log2f(l_run);
+  }
+}
+
+// ============================================================================ backward: dK, dV
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<bf16> a) {
+  using TL = DmaTile<D>;
+  constexpr int BQ = 64, BKV = 128;
+  constexpr int NC = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 qs[2][BQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 dos[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dd_s[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, g = lane >> 5;
+  const int s = a.s;
+  const int nkt = (s + BKV - 1) / BKV;
+  int hk, kt;
+  map_head_tile(blockIdx.x, a.nkv, nkt, false, hk, kt);
+  const int kv0 = kt * BKV;
+  const int kvrow = kv0 + 32 * w + lr;
+  const bf16* Kp = a.k + (int64_t)hk * s * D;
+  const bf16* Vp = a.v + (int64_t)hk * s * D;
+
+  bf16x8 kf[NC], vf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kf[c] = kvrow < s ? ld_frag(Kp + (int64_t)kvrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
+    vf[c] = kvrow < s ? ld_frag(Vp + (int64_t)kvrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
+  }
+
+  f32x16 dkacc[ND], dvacc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) { dkacc[i] = zero16(); dvacc[i] = zero16(); }
+
+  const float sl2 = a.scale_log2, inv_sl2 = 1.f / a.scale_log2;
+  const int nqt = (s + BQ - 1) / BQ;
+  const int qt0 = a.causal ? kv0 / BQ : 0;
+  const int per_head = nqt - qt0;
+  const int nsteps = per_head * a.group;
+
+  float lse_r = 0.f, dd_r = 0.f;
+  auto load_step = [&](int step, int buf) {
+    const int hq = hk * a.group + step / per_head;
+    const int q0 = (qt0 + step % per_head) * BQ;
+    TL::template load<BQ, 4>(qs[buf], a.q + (int64_t)hq * s * D, D, q0, s, w, lane);
+    TL::template load<BQ, 4>(dos[buf], a.dout + (int64_t)hq * D, a.lddo, q0, s, w, lane);
+    if (tid < BQ) {  // stored negated (lse in units of the raw score) to seed the accumulators
+      const int qr = q0 + tid;
+      lse_r = qr < s ? -a.lse[(int64_t)hq * s + qr] * inv_sl2 : -INFINITY;
+      dd_r = qr < s ? -a.dvec[(int64_t)hq * s + qr] : 0.f;
+    }
+  };
+  if (nsteps > 0) {
+    load_step(0, 0);
+    if (tid < BQ) { lse_s[0][tid] = lse_r; dd_s[0][tid] = dd_r; }
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int q0 = (qt0 + step % per_head) * BQ;
+    const int buf = step & 1;
+    if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
+    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // Seeding the accumulators with -lse (score units) and -D_i puts the row
+      // statistics where the products land, with no extra registers.
+      f32x16 sacc, dpacc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 l4 = ld<f32x4>(&lse_s[buf][32 * qb + 8 * k + 4 * g]);
+        const f32x4 d4 = ld<f32x4>(&dd_s[buf][32 * qb + 8 * k + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { sacc[4 * k + j] = l4[j]; dpacc[4 * k + j] = d4[j]; }
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        sacc = mma(TL::frag(qs[buf], 32 * qb + lr, 16 * c + 8 * g), kf[c], sacc);
+        dpacc = mma(TL::frag(dos[buf], 32 * qb + lr, 16 * c + 8 * g), vf[c], dpacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(sacc[r] * sl2);
+        sacc[r] = p;
+        dpacc[r] = p * dpacc[r];
+      }
+      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qg = q0 + 32 * qb + acc_row(r, g);
+          const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1);
+          sacc[r] = masked ? 0.f : sacc[r];
+          dpacc[r] = masked ? 0.f : dpacc[r];
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int cc = 2 * qb + h2;
+        float tp[8], td[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          tp[e] = sacc[8 * h2 + e];
+          td[e] = dpacc[8 * h2 + e];
+        }
+        const bf16x8 pa = pack_frag<bf16>(tp);
+        const bf16x8 dsa = pack_frag<bf16>(td);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          dvacc[i] = mma(pa, TL::tr_frag(dos[buf], cc, i, lane), dvacc[i]);
+          dkacc[i] = mma(dsa, TL::tr_frag(qs[buf], cc, i, lane), dkacc[i]);
+        }
+      }
+    }
+    if (step + 1 < nsteps && tid < BQ) { lse_s[buf ^ 1][tid] = lse_r; dd_s[buf ^ 1][tid] = dd_r; }
+    wait_dma();
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    const int d = 32 * i + lr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kv = kv0 + 32 * w + acc_row(r, g);
+      float dkv = dkacc[i][r] * a.scale;
+      const float pair = shfl_xor(dkv, 1);
+      if (a.rope && kv < s) {
+        const float2 cs = a.rope[(int64_t)kv * (D / 2) + (d >> 1)];
+        dkv = (d & 1) ? (dkv * cs.x - pair * cs.y) : (dkv * cs.x + pair * cs.y);
+      }
+      if (kv < s) {
+        a.dk[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = (bf16)dkv;
+        a.dv[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = (bf16)dvacc[i][r];
+      }
+    }
+  }
+}
+
+// ============================================================================ backward: dQ
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf16> a) {
+  using TL = DmaTile<D>;
+  constexpr int BQ = 128, BKV = 64;
+  constexpr int NC = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 ks[2][BKV * D];
+  __shared__ __attribute__((aligned(1024))) bf16 vs[2][BKV * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 31, g = lane >> 5;
+  const int s = a.s;
+  const int nqt = (s + BQ - 1) / BQ;
+  int hq, qt;
+  map_head_tile(blockIdx.x, a.nh, nqt, a.causal != 0, hq, qt);
+  const int hk = hq / a.group;
+  const int q0 = qt * BQ;
+  const int qrow = q0 + 32 * w + lr;
+  const bf16* Kp = a.k + (int64_t)hk * s * D;
+  const bf16* Vp = a.v + (int64_t)hk * s * D;
+
+  bf16x8 qf[NC], df[NC];
+  const bf16* Qp = a.q + (int64_t)hq * s * D;
+  const bf16* dOp = a.dout + (int64_t)hq * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = qrow < s ? ld_frag(Qp + (int64_t)qrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
+    df[c] = qrow < s ? ld_frag(dOp + (int64_t)qrow * a.lddo + 16 * c + 8 * g) : zero_frag<bf16>();
+  }
+  const float lse_q = qrow < s ? a.lse[(int64_t)hq * s + qrow] : INFINITY;
+  const float dd_q = qrow < s ? a.dvec[(int64_t)hq * s + qrow] : 0.f;
+
+  const int kv_end = a.causal ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const bool wave_active = q0 + 32 * w < s;
+  const int wave_last = min(q0 + 32 * w + 31, s - 1);
+  const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+  const float sl2 = a.scale_log2;
+
+  f32x16 dqacc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) dqacc[i] = zero16();
+
+  if (ntiles > 0) {
+    TL::template load<BKV, 4>(ks[0], Kp, D, 0, s, w, lane);
+    TL::template load<BKV, 4>(vs[0], Vp, D, 0, s, w, lane);
+  }
+  wait_dma();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      TL::template load<BKV, 4>(ks[buf ^ 1], Kp, D, (t + 1) * BKV, s, w, lane);
+      TL::template load<BKV, 4>(vs[buf ^ 1], Vp, D, (t + 1) * BKV, s, w, lane);
+    }
+    if (wave_active && t < wave_tiles) {
+      const int kvb = t * BKV;
+      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          sacc = mma(TL::frag(ks[buf], 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc);
+          dpacc = mma(TL::frag(vs[buf], 32 * sb + lr, 16 * c + 8 * g), df[c], dpacc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+          dpacc[r] = p * (dpacc[r] - dd_q);
+        }
+        if (MASK) {
+          const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb - 32 * sb;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dpacc[r] = (acc_row(r, g) > lim) ? 0.f : dpacc[r];
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int cc = 2 * sb + h2;
+          float td[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) td[e] = dpacc[8 * h2 + e];
+          const bf16x8 dsf = pack_frag<bf16>(td);
+#pragma unroll
+          for (int i = 0; i < ND; ++i) dqacc[i] = mma(TL::tr_frag(ks[buf], cc, i, lane), dsf, dqacc[i]);
+        }
+      }
+    }
+    wait_dma();
+    __syncthreads();
+  }
+
+  if (wave_active && qrow < s) {
+    bf16* out = a.dq + (int64_t)qrow * a.lddq + (int64_t)hq * D;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * i + r4 * 8 + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dqacc[i][4 * r4 + e] * a.scale;
+        if (a.rope) {
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const float2 cs = a.rope[(int64_t)qrow * (D / 2) + ((d0 + e) >> 1)];
+            const float ev = v[e], od = v[e + 1];
+            v[e] = ev * cs.x + od * cs.y;
+            v[e + 1] = -ev * cs.y + od * cs.x;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[d0 + e] = (bf16)v[e];
+      }
+  }
+}
+
+}  // namespace bpt

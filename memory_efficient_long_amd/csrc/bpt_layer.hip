@@ -26,6 +26,7 @@
 
 #include "../../include/bpt.h"
 #include "attention.hpp"
+#include "attention_dma.hpp"
 #include "gemm.hpp"
 #include "rowwise.hpp"
 
@@ -352,8 +353,11 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
-  if (p.D == 128) hipLaunchKernelGGL((attn_fwd_kernel<T, 128>), grid, blk, 0, st, a);
-  else if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
+  if constexpr (sizeof(T) == 2) {
+    if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
+    if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
+  }
+  if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<T, 32>), grid, blk, 0, st, a);
   return check_launch("attn_fwd");
 }
@@ -374,16 +378,28 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
     return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
   {
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DKDV, st);
-    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, sizeof(T) == 2 ? 128 : 64>), gkv, blk, 0, st, a);
-    else if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
-    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), gkv, blk, 0, st, a); done = true; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64>), gkv, blk, 0, st, a); done = true; }
+    }
+    if (!done) {
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
+    }
   }
   BPT_TRY(check_launch("attn_bwd_dkdv"));
   {
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DQ, st);
-    if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, sizeof(T) == 2 ? 128 : 64>), gq, blk, 0, st, a);
-    else if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), gq, blk, 0, st, a); done = true; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<64>), gq, blk, 0, st, a); done = true; }
+    }
+    if (!done) {
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
+    }
   }
   return check_launch("attn_bwd_dq");
 }
