@@ -2,9 +2,11 @@
 // travel global -> LDS by direct LDS loads (global_load_lds_dwordx4: lane l's
 // 16 bytes land at the instruction's LDS base + 16 l), so no register staging
 // and no in-register transposes are needed. Tiles are row-major, unpadded,
-// with the 16-byte chunks of row r XOR-permuted by f(r) = 2 (r & 3) +
-// ((r >> 2) & 1): eight consecutive rows (a row-operand fragment read) and
-// four consecutive rows (a transpose read) fall on distinct banks. Operands
+// with the 16-byte chunks of row r XOR-permuted by f(r) (see DmaTile) so
+// that both read forms are free of bank conflicts on the 64-bank LDS: a
+// 16-byte row-fragment read serves 16 lanes (16 consecutive rows, one chunk
+// each) per cycle, a transpose read 32 lanes (4 consecutive rows, 64
+// contiguous bytes each). Operands
 // that need the transposed tile (V^T in the forward, dO^T and Q^T in the
 // dK/dV pass, K^T in the dQ pass) are read with ds_read_b64_tr_b16, which,
 // within each 16-lane group, gives lane i element (i % 4) of the 8-byte piece
@@ -27,8 +29,16 @@ template <int D>
 struct DmaTile {
   static constexpr int RB = D * 2;   // row bytes (bf16)
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  static_assert(CPR >= 8, "head_dim must be >= 64");
-  __device__ static __forceinline__ int f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  // D = 128 (one row per 256-byte bank line): f = 4 (r & 3) + ((r >> 2) & 3)
+  // is a bijection on 16 consecutive rows, and its high two bits separate
+  // the 4-chunk groups of 4 consecutive rows. D = 64 (two rows per line):
+  // f = 4 ((r >> 1) & 1) + ((r >> 2) & 3) does the same with the row parity
+  // selecting the half line. Both satisfy f(r + 8) = f(r) ^ 2, so the
+  // second half of a transpose fragment sits at the first address ^ 32.
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
   __device__ static __forceinline__ int off(int r, int chunk) {
     return r * RB + ((chunk ^ f(r)) << 4);
   }
@@ -66,19 +76,19 @@ struct DmaTile {
     const int li = lane & 15, g = lane >> 5;
     const int col = 32 * i + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
     const int r0 = 16 * cc + 4 * g + (li >> 2);
-    const int pc = ((col >> 3) ^ f(r0)) << 4;  // f(r0 + 8) == f(r0)
+    const int pc = ((col >> 3) ^ f(r0)) << 4;
     const int pb = ((col >> 2) & 1) << 3;
-    const char* b0 = (const char*)tile + r0 * RB + pc + pb;
+    // Tiles are 1024-byte aligned and rows RB-aligned, so XOR-ing the byte
+    // address by 32 flips bit 1 of the chunk index: f(r0 + 8) = f(r0) ^ 2.
+    const uint32_t a0 = (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)tile) +
+                        r0 * RB + pc + pb;
+    const uint32_t a1 = (a0 ^ 32u) + 8 * RB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)b0);
+        (__attribute__((address_space(3))) s16x4*)(size_t)a0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(b0 + 8 * RB));
-    u32x4 v;
-    v[0] = (unsigned)(unsigned short)lo[0] | ((unsigned)(unsigned short)lo[1] << 16);
-    v[1] = (unsigned)(unsigned short)lo[2] | ((unsigned)(unsigned short)lo[3] << 16);
-    v[2] = (unsigned)(unsigned short)hi[0] | ((unsigned)(unsigned short)hi[1] << 16);
-    v[3] = (unsigned)(unsigned short)hi[2] | ((unsigned)(unsigned short)hi[3] << 16);
-    return __builtin_bit_cast(bf16x8, v);
+        (__attribute__((address_space(3))) s16x4*)(size_t)a1);
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
   }
 };
 

@@ -27,6 +27,7 @@
 #include "../../include/bpt.h"
 #include "attention.hpp"
 #include "attention_dma.hpp"
+#include "gemm_dma.hpp"
 #include "gemm.hpp"
 #include "rowwise.hpp"
 
@@ -263,8 +264,18 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
   if (!ok) return fail(BPT_EUNSUPPORTED, std::string("gemm layout invariant: ") + what);
   if (M == 0 || N == 0) return BPT_OK;
   TimedLaunch tl(BPT_KERNEL_GEMM, st);
-  // 128 x 128 tiles, 4 waves of 64 x 64: two workgroups per CU (8 waves) hide
-  // latency better than larger single-workgroup tiles on the measured shapes.
+  if constexpr (sizeof(T) == 2) {
+    if (K % 64 == 0) {
+      // Direct-to-LDS pipeline: 128 x 128 x 64 tiles, two stages, two
+      // workgroups per CU.
+      const int64_t nt = ((M + 127) / 128) * ((N + 127) / 128);
+      hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, 128, 128, 64, 2, 64, 64, Epi>), dim3((unsigned)nt),
+                         dim3(256), 0, st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+      return check_launch(what);
+    }
+  }
+  // Register-staged path (fp32, and bf16 with K not a multiple of 64):
+  // 128 x 128 tiles, 4 waves of 64 x 64, two workgroups per CU.
   const bool even = M % 128 == 0 && N % 128 == 0 && K % BKK == 0;
   launch_gemm<T, AK, BK, 128, 128, BKK, 64, 64>(st, A, lda, B, ldb, M, N, K, epi, even);
   return check_launch(what);

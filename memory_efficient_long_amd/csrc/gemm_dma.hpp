@@ -1,0 +1,238 @@
+// bf16 MFMA GEMM fed by direct global -> LDS loads, same contract and
+// epilogues as gemm_kernel in gemm.hpp (C[m, n] = sum_k A(m, k) B(n, k)).
+//
+// Each operand tile is stored in LDS in its global orientation, unpadded:
+//   K-major operand (A(m, k) = A[m * lda + k]): BMN rows of BK k values;
+//     fragments (one row, 8 consecutive k) are single 16-byte LDS reads.
+//   MN-major operand (A(m, k) = A[k * lda + m]): BK rows of BMN values;
+//     fragments come from two ds_read_b64_tr_b16, each giving a lane four
+//     consecutive k of its column.
+// Both forms hand lane (r = lane % 32, g = lane / 32) the reduction indices
+// 16 kk + 8 g + {0..7}, so any pair of layouts feeds the same MFMA.
+//
+// global_load_lds moves 16 bytes per lane into LDS at the instruction's base
+// + 16 * lane, so the bank swizzle (16-byte chunks XOR-permuted per row) is
+// applied by choosing which global chunk each lane fetches. Nothing is staged
+// in registers, which lets the pipeline run STAGES deep: the loads of step
+// kt + STAGES - 1 are in flight while step kt computes.
+//
+// Requirements (checked by the host): K % BK == 0, rows of K-major operands
+// and the contiguous extent of MN-major operands multiple of 8 elements,
+// 16-byte aligned base pointers and leading dimensions. M and N tails are
+// handled by clamping the fetched rows / columns (the extra outputs are not
+// stored).
+#pragma once
+
+#include "gemm.hpp"
+
+namespace bpt {
+
+namespace gdma {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt fields left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// K-major tile: R rows x BK bf16.
+template <int R, int BK>
+struct KTile {
+  static constexpr int RB = BK * 2;
+  static constexpr int CPR = BK / 8;
+  static constexpr int BYTES = R * RB;
+  static constexpr int RPL = 16 / CPR;  // rows per 256-byte bank line
+  // A 16-byte fragment read serves 16 lanes (16 consecutive rows) per cycle:
+  // f is a bijection on the bank-line index of 16 consecutive rows.
+  __device__ static __forceinline__ int f(int r) { return (r / RPL) & (CPR - 1); }
+
+  // Loads rows [row0, row0 + R) (clamped to rlim - 1), k in [k0, k0 + BK).
+  template <int NW>
+  __device__ static __forceinline__ void load(char* tile, const bf16* src, int64_t ld, int row0,
+                                              int rlim, int k0, int w, int lane) {
+    constexpr int PERW = BYTES / 1024 / NW;
+    static_assert(PERW >= 1 && BYTES % (1024 * NW) == 0, "tile split");
+#pragma unroll
+    for (int m = 0; m < PERW; ++m) {
+      const int base = (w * PERW + m) * 1024;
+      const int q = (base >> 4) + lane;
+      const int r = q / CPR, p = q % CPR;
+      const int gr = min(row0 + r, rlim - 1);
+      dma16(src + (int64_t)gr * ld + k0 + ((p ^ f(r)) << 3), tile + base);
+    }
+  }
+  __device__ static __forceinline__ bf16x8 frag(const char* tile, int r, int kc) {
+    return ld<bf16x8>(tile + r * RB + ((kc ^ f(r)) << 4));
+  }
+};
+
+// MN-major tile: BK rows (k) x C bf16 columns.
+template <int BK, int C>
+struct NTile {
+  static constexpr int RB = C * 2;
+  static constexpr int CPR = C / 8;
+  static constexpr int BYTES = BK * RB;
+  static_assert(CPR >= 8, "at least 64 columns");
+  // A transpose read serves 32 lanes (4 consecutive rows x 64 contiguous
+  // bytes) per cycle: the rows' 4-chunk groups must land on distinct banks.
+  __device__ static __forceinline__ int f(int r) { return (r & 3) << 2; }
+
+  template <int NW>
+  __device__ static __forceinline__ void load(char* tile, const bf16* src, int64_t ld, int col0,
+                                              int clim, int k0, int w, int lane) {
+    constexpr int PERW = BYTES / 1024 / NW;
+    static_assert(PERW >= 1 && BYTES % (1024 * NW) == 0, "tile split");
+#pragma unroll
+    for (int m = 0; m < PERW; ++m) {
+      const int base = (w * PERW + m) * 1024;
+      const int q = (base >> 4) + lane;
+      const int r = q / CPR, p = q % CPR;
+      const int gc = min(col0 + ((p ^ f(r)) << 3), clim - 8);
+      dma16(src + (int64_t)(k0 + r) * ld + gc, tile + base);
+    }
+  }
+  // Column n0 + (lane % 32), k = 16 kk + 8 g + {0..7}.
+  __device__ static __forceinline__ bf16x8 frag(const char* tile, int kk, int n0, int lane) {
+    const int li = lane & 15, g = lane >> 5;
+    const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+    const int r0 = 16 * kk + 8 * g + (li >> 2);
+    const int off = ((((col >> 3) ^ f(r0)) << 4)) | (((col >> 2) & 1) << 3);  // f(r0 + 4) == f(r0)
+    const char* b0 = tile + r0 * RB + off;
+    const s16x4 lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)b0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(b0 + 4 * RB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+  }
+};
+
+template <bool KMAJ, int R, int BK>
+struct Operand;
+template <int R, int BK>
+struct Operand<true, R, BK> {
+  using Tile = KTile<R, BK>;
+  __device__ static __forceinline__ void load(char* t, const bf16* src, int64_t ld, int rc0,
+                                              int lim, int k0, int w, int lane) {
+    Tile::template load<4>(t, src, ld, rc0, lim, k0, w, lane);
+  }
+  // Fragment for rows r0 + (lane % 32), reduction step kk.
+  __device__ static __forceinline__ bf16x8 frag(const char* t, int kk, int r0, int lane) {
+    return Tile::frag(t, r0 + (lane & 31), 2 * kk + (lane >> 5));
+  }
+};
+template <int R, int BK>
+struct Operand<false, R, BK> {
+  using Tile = NTile<BK, R>;
+  __device__ static __forceinline__ void load(char* t, const bf16* src, int64_t ld, int rc0,
+                                              int lim, int k0, int w, int lane) {
+    Tile::template load<4>(t, src, ld, rc0, lim, k0, w, lane);
+  }
+  __device__ static __forceinline__ bf16x8 frag(const char* t, int kk, int r0, int lane) {
+    return Tile::frag(t, kk, r0, lane);
+  }
+};
+
+}  // namespace gdma
+
+template <bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int STAGES, int WM, int WN, class Epi>
+__global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                       const bf16* __restrict__ B, int64_t ldb,
+                                                       int M, int N, int K, Epi epi) {
+  using OA = gdma::Operand<A_KMAJ, BM, BK>;
+  using OB = gdma::Operand<B_KMAJ, BN, BK>;
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
+  constexpr int LOADS = SBYTES / 1024 / 4;  // direct loads per wave per stage
+  constexpr int WGN = BN / WN;
+  static_assert((BM / WM) * (BN / WN) == 4, "4 waves per workgroup");
+  constexpr int FM = WM / 32, FN = WN / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SBYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5;
+
+  // Same XCD-grouped tile order as gemm_kernel.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int nt = tiles_m * tiles_n;
+  int tile;
+  {
+    const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+    const int q = nt >> 3, rem = nt & 7;
+    tile = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
+  }
+  constexpr int GROUP = 8;
+  const int group = tile / (GROUP * tiles_n);
+  const int first_m = group * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (tile % (GROUP * tiles_n)) % gsz;
+  const int tn = (tile % (GROUP * tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (w / WGN) * WM, wn0 = (w % WGN) * WN;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
+
+  const int nk = K / BK;
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % STAGES) * SBYTES;
+    OA::load(st, A, lda, m0, M, kt * BK, w, lane);
+    OB::load(st + ABYTES, B, ldb, n0, N, kt * BK, w, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt is complete once at most the loads of the stages issued after
+    // it remain in flight; the tail waits for everything.
+    if (kt + STAGES - 2 < nk) gdma::wait_vm<(STAGES - 2) * LOADS>();
+    else gdma::wait_vm<0>();
+    __syncthreads();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const char* As = smem + (kt % STAGES) * SBYTES;
+    const char* Bs = As + ABYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = OA::frag(As, kk, wm0 + 32 * i, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = OB::frag(Bs, kk, wn0 + 32 * j, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  const int lr = lane & 31;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn0 + 32 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm0 + 32 * i + acc_row(r, g);
+        float v = acc[i][j][r];
+        float vp = 0.f;
+        if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
+        if (row < M && col < N) epi(row, col, v, vp);
+      }
+    }
+}
+
+}  // namespace bpt
