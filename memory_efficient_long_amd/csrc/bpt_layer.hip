@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -249,6 +250,34 @@ void launch_gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ld
                        dim3(256), 0, st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <bool AK, bool BK, int BM, int BN, int BKK, int ST, int WM, int WN, int NW, class Epi>
+void launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
+                     int64_t M, int64_t N, int64_t K, const Epi& epi) {
+  constexpr int kLds = ST * (BM + BN) * BKK * 2;
+  auto kern = gemm_dma_kernel<AK, BK, BM, BN, BKK, ST, WM, WN, NW, Epi>;
+  static std::once_flag attr_once;  // per instantiation
+  std::call_once(attr_once, [&] {
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  });
+  const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nt), dim3(64 * NW), kLds, st, A, lda, B, ldb, (int)M,
+                     (int)N, (int)K, epi);
+}
+
 template <typename T, bool AK, bool BK, class Epi>
 bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
                 int64_t N, int64_t K, const Epi& epi, const char* what) {
@@ -266,11 +295,16 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
   TimedLaunch tl(BPT_KERNEL_GEMM, st);
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0) {
-      // Direct-to-LDS pipeline: 128 x 128 x 64 tiles, two stages, two
+      // Direct-to-LDS pipelines. Shapes with at least one 256 x 256 tile per
+      // CU use 8 waves of 64 x 128 (half the L2 -> LDS traffic per flop of a
+      // 128 x 128 tile); smaller outputs use 128 x 128 tiles of 4 waves, two
       // workgroups per CU.
-      const int64_t nt = ((M + 127) / 128) * ((N + 127) / 128);
-      hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, 128, 128, 64, 2, 64, 64, Epi>), dim3((unsigned)nt),
-                         dim3(256), 0, st, A, lda, B, ldb, (int)M, (int)N, (int)K, epi);
+      const int64_t nt256 = ((M + 255) / 256) * ((N + 255) / 256);
+      if (nt256 >= device_cus()) {
+        launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, epi);
+      } else {
+        launch_gemm_dma<AK, BK, 128, 128, 64, 2, 64, 64, 4>(st, A, lda, B, ldb, M, N, K, epi);
+      }
       return check_launch(what);
     }
   }

@@ -31,17 +31,20 @@ namespace gdma {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
 // Wait until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt fields left at their maxima, i.e. not waited on).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One direct load: 16 bytes per lane from a wave-uniform base plus a per-lane
+// 32-bit byte offset (the scalar-base addressing form, so the only per-load
+// vector work is none), into LDS at the uniform address lds.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sbase + voff),
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 // K-major tile: R rows x BK bf16.
@@ -55,21 +58,34 @@ struct KTile {
   // f is a bijection on the bank-line index of 16 consecutive rows.
   __device__ static __forceinline__ int f(int r) { return (r / RPL) & (CPR - 1); }
 
-  // Loads rows [row0, row0 + R) (clamped to rlim - 1), k in [k0, k0 + BK).
+  // Per-lane byte offsets (relative to the tile's first row) of the rows
+  // [row0, row0 + R) clamped to rlim - 1; the k offset is added per step.
+  // NW waves share the tile.
   template <int NW>
-  __device__ static __forceinline__ void load(char* tile, const bf16* src, int64_t ld, int row0,
-                                              int rlim, int k0, int w, int lane) {
-    constexpr int PERW = BYTES / 1024 / NW;
+  struct Loader {
+    static constexpr int PERW = BYTES / 1024 / NW;  // loads per wave
     static_assert(PERW >= 1 && BYTES % (1024 * NW) == 0, "tile split");
+    const char* base;
+    int64_t ld_bytes;
+    uint32_t voff[PERW];
+    __device__ __forceinline__ Loader(const bf16* src, int64_t ld, int row0, int rlim, int w,
+                                      int lane) {
+      base = (const char*)src + (int64_t)row0 * ld * 2;
+      ld_bytes = ld * 2;
 #pragma unroll
-    for (int m = 0; m < PERW; ++m) {
-      const int base = (w * PERW + m) * 1024;
-      const int q = (base >> 4) + lane;
-      const int r = q / CPR, p = q % CPR;
-      const int gr = min(row0 + r, rlim - 1);
-      dma16(src + (int64_t)gr * ld + k0 + ((p ^ f(r)) << 3), tile + base);
+      for (int m = 0; m < PERW; ++m) {
+        const int q = (w * PERW + m) * 64 + lane;
+        const int r = q / CPR, p = q % CPR;
+        const int rr = min(r, rlim - 1 - row0);
+        voff[m] = (uint32_t)((int64_t)rr * ld * 2) + (uint32_t)((p ^ f(r)) << 4);
+      }
     }
-  }
+    __device__ __forceinline__ void issue(char* tile, int k0, int w) const {
+      const char* sb = base + (int64_t)k0 * 2;
+#pragma unroll
+      for (int m = 0; m < PERW; ++m) dma16(sb, voff[m], tile + (w * PERW + m) * 1024);
+    }
+  };
   __device__ static __forceinline__ bf16x8 frag(const char* tile, int r, int kc) {
     return ld<bf16x8>(tile + r * RB + ((kc ^ f(r)) << 4));
   }
@@ -87,19 +103,30 @@ struct NTile {
   __device__ static __forceinline__ int f(int r) { return (r & 3) << 2; }
 
   template <int NW>
-  __device__ static __forceinline__ void load(char* tile, const bf16* src, int64_t ld, int col0,
-                                              int clim, int k0, int w, int lane) {
-    constexpr int PERW = BYTES / 1024 / NW;
+  struct Loader {
+    static constexpr int PERW = BYTES / 1024 / NW;
     static_assert(PERW >= 1 && BYTES % (1024 * NW) == 0, "tile split");
+    const char* base;
+    int64_t ld_bytes;
+    uint32_t voff[PERW];
+    __device__ __forceinline__ Loader(const bf16* src, int64_t ld, int col0, int clim, int w,
+                                      int lane) {
+      base = (const char*)src + (int64_t)col0 * 2;
+      ld_bytes = ld * 2;
 #pragma unroll
-    for (int m = 0; m < PERW; ++m) {
-      const int base = (w * PERW + m) * 1024;
-      const int q = (base >> 4) + lane;
-      const int r = q / CPR, p = q % CPR;
-      const int gc = min(col0 + ((p ^ f(r)) << 3), clim - 8);
-      dma16(src + (int64_t)(k0 + r) * ld + gc, tile + base);
+      for (int m = 0; m < PERW; ++m) {
+        const int q = (w * PERW + m) * 64 + lane;
+        const int r = q / CPR, p = q % CPR;
+        const int c = min((p ^ f(r)) << 3, clim - 8 - col0);
+        voff[m] = (uint32_t)((int64_t)r * ld * 2) + (uint32_t)(c * 2);
+      }
     }
-  }
+    __device__ __forceinline__ void issue(char* tile, int k0, int w) const {
+      const char* sb = base + (int64_t)k0 * ld_bytes;
+#pragma unroll
+      for (int m = 0; m < PERW; ++m) dma16(sb, voff[m], tile + (w * PERW + m) * 1024);
+    }
+  };
   // Column n0 + (lane % 32), k = 16 kk + 8 g + {0..7}.
   __device__ static __forceinline__ bf16x8 frag(const char* tile, int kk, int n0, int lane) {
     const int li = lane & 15, g = lane >> 5;
@@ -121,10 +148,8 @@ struct Operand;
 template <int R, int BK>
 struct Operand<true, R, BK> {
   using Tile = KTile<R, BK>;
-  __device__ static __forceinline__ void load(char* t, const bf16* src, int64_t ld, int rc0,
-                                              int lim, int k0, int w, int lane) {
-    Tile::template load<4>(t, src, ld, rc0, lim, k0, w, lane);
-  }
+  template <int NW>
+  using Loader = typename Tile::template Loader<NW>;
   // Fragment for rows r0 + (lane % 32), reduction step kk.
   __device__ static __forceinline__ bf16x8 frag(const char* t, int kk, int r0, int lane) {
     return Tile::frag(t, r0 + (lane & 31), 2 * kk + (lane >> 5));
@@ -133,10 +158,8 @@ struct Operand<true, R, BK> {
 template <int R, int BK>
 struct Operand<false, R, BK> {
   using Tile = NTile<BK, R>;
-  __device__ static __forceinline__ void load(char* t, const bf16* src, int64_t ld, int rc0,
-                                              int lim, int k0, int w, int lane) {
-    Tile::template load<4>(t, src, ld, rc0, lim, k0, w, lane);
-  }
+  template <int NW>
+  using Loader = typename Tile::template Loader<NW>;
   __device__ static __forceinline__ bf16x8 frag(const char* t, int kk, int r0, int lane) {
     return Tile::frag(t, kk, r0, lane);
   }
@@ -144,21 +167,24 @@ struct Operand<false, R, BK> {
 
 }  // namespace gdma
 
-template <bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int STAGES, int WM, int WN, class Epi>
-__global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ A, int64_t lda,
+// NW waves (64 NW threads) arranged (BM / WM) x (BN / WN); LDS (STAGES stages
+// of the A and B tiles) is dynamic: STAGES * (BM + BN) * BK * 2 bytes.
+template <bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int STAGES, int WM, int WN, int NW,
+          class Epi>
+__global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, int64_t lda,
                                                        const bf16* __restrict__ B, int64_t ldb,
                                                        int M, int N, int K, Epi epi) {
   using OA = gdma::Operand<A_KMAJ, BM, BK>;
   using OB = gdma::Operand<B_KMAJ, BN, BK>;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
-  constexpr int LOADS = SBYTES / 1024 / 4;  // direct loads per wave per stage
+  constexpr int LOADS = SBYTES / 1024 / NW;  // direct loads per wave per stage
   constexpr int WGN = BN / WN;
-  static_assert((BM / WM) * (BN / WN) == 4, "4 waves per workgroup");
+  static_assert((BM / WM) * (BN / WN) == NW, "wave grid");
   constexpr int FM = WM / 32, FN = WN / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SBYTES];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
 
   // Same XCD-grouped tile order as gemm_kernel.
@@ -186,10 +212,12 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ 
     for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
 
   const int nk = K / BK;
+  const typename OA::template Loader<NW> la(A, lda, m0, M, w, lane);
+  const typename OB::template Loader<NW> lb(B, ldb, n0, N, w, lane);
   auto issue = [&](int kt) {
     char* st = smem + (kt % STAGES) * SBYTES;
-    OA::load(st, A, lda, m0, M, kt * BK, w, lane);
-    OB::load(st + ABYTES, B, ldb, n0, N, kt * BK, w, lane);
+    la.issue(st, kt * BK, w);
+    lb.issue(st + ABYTES, kt * BK, w);
   };
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -204,17 +232,26 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(const bf16* __restrict__ 
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const char* As = smem + (kt % STAGES) * SBYTES;
     const char* Bs = As + ABYTES;
+    // Fragments of reduction step kk + 1 are read while step kk's MFMAs run.
+    constexpr int KK = BK / 16;
+    bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i) af[0][i] = OA::frag(As, 0, wm0 + 32 * i, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = OA::frag(As, kk, wm0 + 32 * i, lane);
+    for (int j = 0; j < FN; ++j) bfr[0][j] = OB::frag(Bs, 0, wn0 + 32 * j, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = OB::frag(Bs, kk, wn0 + 32 * j, lane);
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[cur ^ 1][i] = OA::frag(As, kk + 1, wm0 + 32 * i, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[cur ^ 1][j] = OB::frag(Bs, kk + 1, wn0 + 32 * j, lane);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mma(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma(af[cur][i], bfr[cur][j], acc[i][j]);
     }
   }
 
