@@ -101,7 +101,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="gpt1b-s128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-len", type=int, default=2048)
+    ap.add_argument("--cpu-sample-len", type=int, default=8192)
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -210,7 +210,9 @@ def main() -> int:
     avg_ms = dom_ms / max(dom_n, 1)
     per_launch_flops = fl[dom] / max(dom_n / args.steps, 1)
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
-    kernel_name = dom + "_kernel"
+    # bf16 with head_dim 64 / 128 runs the direct-to-LDS attention kernels.
+    dma = sh.dtype == "bf16" and sh.head_dim in (64, 128)
+    kernel_name = dom + ("_dma_kernel" if dma else "_kernel")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": load_traffic(kernel_name, sh.name), "kernel": kernel_name,
