@@ -90,7 +90,98 @@ struct DmaTile {
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
   }
+
+  // ---- Fragment reads from a per-lane constant base: the chunk permutation
+  // is an XOR on bits that lie below the row stride, so every fragment of a
+  // lane is its base XOR a compile-time constant plus a constant offset (one
+  // base register per read form instead of one address per fragment).
+  //   row fragment (row 32 blk + lane % 32, elements 16 c + 8 g .. + 7):
+  //     tile + 32 blk RB + (rf ^ 32 c)
+  //   transpose fragment (as tr_frag(cc, i)):
+  //     a0 = tile + 16 cc RB + (tr ^ 64 i), a1 = (a0 ^ 32) + 8 RB
+  __device__ static __forceinline__ uint32_t rf_base(int lane) {
+    const int lr = lane & 31, g = lane >> 5, F = f(lr);
+    return lr * RB + 32 * (F >> 1) + 16 * (g ^ (F & 1));
+  }
+  __device__ static __forceinline__ uint32_t tr_base(int lane) {
+    const int li = lane & 15, g = lane >> 5, half = (lane >> 4) & 1;
+    const int r = 4 * g + (li >> 2), F = f(r), x = 2 * half + ((li & 3) >> 1);
+    return r * RB + 64 * (F >> 2) + 16 * (x ^ (F & 3)) + 8 * (li & 1);
+  }
+  __device__ static __forceinline__ bf16x8 frag_at(uint32_t tile, uint32_t rf, int blk, int c) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(tile + 32 * blk * RB +
+                                                                       (rf ^ (32u * c)));
+  }
+  __device__ static __forceinline__ bf16x8 tr_at(uint32_t tile, uint32_t tr, int cc, int i) {
+    const uint32_t a0 = tile + 16 * cc * RB + (tr ^ (64u * i));
+    const uint32_t a1 = (a0 ^ 32u) + 8 * RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(size_t)a0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(size_t)a1);
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+  }
+
+  // ---- Direct loads of R-row tiles (NW waves) with a per-lane constant
+  // offset: load m of wave w covers rows brow = (w PERW + m) RPI + lane / CPR,
+  // and f(brow + j) = f(brow) ^ f(j) for j < RPI, so the global chunk is
+  // (lane % CPR) ^ f(lane / CPR) ^ f(brow) with the last term wave-uniform.
+  // Requires the row stride (in bytes) to be a multiple of RB.
+  template <int R, int NW>
+  struct Loader {
+    static constexpr int PERW = R * RB / 1024 / NW, RPI = 1024 / RB;
+    static_assert(PERW >= 1 && R * RB % (1024 * NW) == 0, "tile split");
+    uint32_t l0;
+    int64_t ldb;
+    __device__ __forceinline__ Loader(int64_t ld, int lane) : ldb(ld * 2) {
+      const int j = lane / CPR;
+      l0 = (uint32_t)(j * ldb) + 16u * ((lane % CPR) ^ f(j));
+    }
+    // Rows [row0, row0 + R) of src into the tile at LDS address `tile`; rows
+    // at or past rlim repeat row rlim - 1 (masked by the caller).
+    __device__ __forceinline__ void issue(uint32_t tile, const bf16* src, int row0, int rlim, int w,
+                                          int lane) const {
+      // The empty asm statements make the lane values opaque at each call, so
+      // the per-load offsets are recomputed here (one VALU op each) rather
+      // than hoisted out of the caller's loop into registers of their own.
+      if (row0 + R <= rlim) {
+        uint32_t l = l0;
+        asm volatile("" : "+v"(l));
+        const char* base = (const char*)src + (int64_t)row0 * ldb;
+#pragma unroll
+        for (int m = 0; m < PERW; ++m) {
+          const int brow = (w * PERW + m) * RPI;
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(base + brow * ldb +
+                                                              (l ^ (16u * f(brow)))),
+              (__attribute__((address_space(3))) void*)(size_t)(tile + (w * PERW + m) * 1024), 16,
+              0, 0);
+        }
+      } else {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int m = 0; m < PERW; ++m) {
+          const int o = (w * PERW + m) * 1024 + 16 * ln;
+          const int r = o / RB, p = (o % RB) >> 4;
+          const int gr = min(row0 + r, rlim - 1);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)((const char*)src + gr * ldb +
+                                                              ((p ^ f(r)) << 4)),
+              (__attribute__((address_space(3))) void*)(size_t)(tile + (w * PERW + m) * 1024), 16,
+              0, 0);
+        }
+      }
+    }
+  };
 };
+
+// LDS byte address of a shared-memory object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
+}
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -102,8 +193,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   constexpr int NC = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(1024))) bf16 ks[2][BKV * D];
   __shared__ __attribute__((aligned(1024))) bf16 vs[2][BKV * D];
+  constexpr uint32_t TB = BKV * D * 2;  // tile bytes
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, g = lane >> 5;
   const int s = a.s;
   const int nqt = (s + BQ - 1) / BQ;
@@ -133,18 +225,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
 
+  const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
+  uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
+  const typename TL::template Loader<BKV, 4> kvld(D, lane);
   if (ntiles > 0) {
-    TL::template load<BKV, 4>(ks[0], Kp, D, 0, s, w, lane);
-    TL::template load<BKV, 4>(vs[0], Vp, D, 0, s, w, lane);
+    kvld.issue(ksa, Kp, 0, s, w, lane);
+    kvld.issue(vsa, Vp, 0, s, w, lane);
   }
   wait_dma();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
+    // Opaque to the optimiser: keeps the per-fragment XORs inside the loop
+    // instead of one hoisted address register per fragment.
+    asm volatile("" : "+v"(rf), "+v"(trb));
     if (t + 1 < ntiles) {
-      TL::template load<BKV, 4>(ks[buf ^ 1], Kp, D, (t + 1) * BKV, s, w, lane);
-      TL::template load<BKV, 4>(vs[buf ^ 1], Vp, D, (t + 1) * BKV, s, w, lane);
+      kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
+      kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
     }
     if (wave_active && t < wave_tiles) {
       const int kvb = t * BKV;
@@ -154,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
-          sacc[sb] = mma(TL::frag(ks[buf], 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc[sb]);
+          sacc[sb] = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc[sb]);
       if (MASK) {  // wave-uniform; keys past min(query, s - 1) get -inf
         const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb;
 #pragma unroll
@@ -196,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
         for (int e = 0; e < 8; ++e) tmp[e] = sacc[cc >> 1][8 * (cc & 1) + e];
         const bf16x8 pf = pack_frag<bf16>(tmp);
 #pragma unroll
-        for (int i = 0; i < ND; ++i) oacc[i] = mma(TL::tr_frag(vs[buf], cc, i, lane), pf, oacc[i]);
+        for (int i = 0; i < ND; ++i) oacc[i] = mma(TL::tr_at(vsa + buf * TB, trb, cc, i), pf, oacc[i]);
       }
     }
     wait_dma();
@@ -227,9 +325,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   __shared__ __attribute__((aligned(1024))) bf16 qs[2][BQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 dos[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  constexpr uint32_t TB = BQ * D * 2;  // tile bytes
   __shared__ __attribute__((aligned(16))) float dd_s[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, g = lane >> 5;
   const int s = a.s;
   const int nkt = (s + BKV - 1) / BKV;
@@ -257,21 +356,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const int per_head = nqt - qt0;
   const int nsteps = per_head * a.group;
 
+  // Row statistics of the next step: loaded raw (before the tile loads, so
+  // waiting for them never waits for the tiles) and converted when stored.
   float lse_r = 0.f, dd_r = 0.f;
+  bool valid_r = false;
+  const uint32_t qsa = lds_addr(&qs[0][0]), dosa = lds_addr(&dos[0][0]);
+  uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
+  const typename TL::template Loader<BQ, 4> qld(D, lane), dold(a.lddo, lane);
   auto load_step = [&](int step, int buf) {
     const int hq = hk * a.group + step / per_head;
     const int q0 = (qt0 + step % per_head) * BQ;
-    TL::template load<BQ, 4>(qs[buf], a.q + (int64_t)hq * s * D, D, q0, s, w, lane);
-    TL::template load<BQ, 4>(dos[buf], a.dout + (int64_t)hq * D, a.lddo, q0, s, w, lane);
-    if (tid < BQ) {  // stored negated (lse in units of the raw score) to seed the accumulators
+    if (tid < BQ) {
       const int qr = q0 + tid;
-      lse_r = qr < s ? -a.lse[(int64_t)hq * s + qr] * inv_sl2 : -INFINITY;
-      dd_r = qr < s ? -a.dvec[(int64_t)hq * s + qr] : 0.f;
+      valid_r = qr < s;
+      lse_r = valid_r ? a.lse[(int64_t)hq * s + qr] : 0.f;
+      dd_r = valid_r ? a.dvec[(int64_t)hq * s + qr] : 0.f;
+    }
+    qld.issue(qsa + buf * TB, a.q + (int64_t)hq * s * D, q0, s, w, lane);
+    dold.issue(dosa + buf * TB, a.dout + (int64_t)hq * D, q0, s, w, lane);
+  };
+  // Stored negated (the LSE in units of the raw score) to seed the S and dP
+  // accumulators; rows past the end get -inf (P = 0) and 0.
+  auto store_stats = [&](int buf) {
+    if (tid < BQ) {
+      lse_s[buf][tid] = valid_r ? -lse_r * inv_sl2 : -INFINITY;
+      dd_s[buf][tid] = valid_r ? -dd_r : 0.f;
     }
   };
   if (nsteps > 0) {
     load_step(0, 0);
-    if (tid < BQ) { lse_s[0][tid] = lse_r; dd_s[0][tid] = dd_r; }
+    store_stats(0);
   }
   wait_dma();
   __syncthreads();
@@ -279,6 +393,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   for (int step = 0; step < nsteps; ++step) {
     const int q0 = (qt0 + step % per_head) * BQ;
     const int buf = step & 1;
+    asm volatile("" : "+v"(rf), "+v"(trb));  // see the forward kernel
     if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
     const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
 #pragma unroll
@@ -295,8 +410,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc = mma(TL::frag(qs[buf], 32 * qb + lr, 16 * c + 8 * g), kf[c], sacc);
-        dpacc = mma(TL::frag(dos[buf], 32 * qb + lr, 16 * c + 8 * g), vf[c], dpacc);
+        sacc = mma(TL::frag_at(qsa + buf * TB, rf, qb, c), kf[c], sacc);
+        dpacc = mma(TL::frag_at(dosa + buf * TB, rf, qb, c), vf[c], dpacc);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -326,12 +441,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         const bf16x8 dsa = pack_frag<bf16>(td);
 #pragma unroll
         for (int i = 0; i < ND; ++i) {
-          dvacc[i] = mma(pa, TL::tr_frag(dos[buf], cc, i, lane), dvacc[i]);
-          dkacc[i] = mma(dsa, TL::tr_frag(qs[buf], cc, i, lane), dkacc[i]);
+          dvacc[i] = mma(pa, TL::tr_at(dosa + buf * TB, trb, cc, i), dvacc[i]);
+          dkacc[i] = mma(dsa, TL::tr_at(qsa + buf * TB, trb, cc, i), dkacc[i]);
         }
       }
     }
-    if (step + 1 < nsteps && tid < BQ) { lse_s[buf ^ 1][tid] = lse_r; dd_s[buf ^ 1][tid] = dd_r; }
+    if (step + 1 < nsteps) store_stats(buf ^ 1);
     wait_dma();
     __syncthreads();
   }
@@ -364,8 +479,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   constexpr int NC = D / 16, ND = D / 32;
   __shared__ __attribute__((aligned(1024))) bf16 ks[2][BKV * D];
   __shared__ __attribute__((aligned(1024))) bf16 vs[2][BKV * D];
+  constexpr uint32_t TB = BKV * D * 2;  // tile bytes
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, g = lane >> 5;
   const int s = a.s;
   const int nqt = (s + BQ - 1) / BQ;
@@ -399,18 +515,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
 #pragma unroll
   for (int i = 0; i < ND; ++i) dqacc[i] = zero16();
 
+  const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
+  uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
+  const typename TL::template Loader<BKV, 4> kvld(D, lane);
   if (ntiles > 0) {
-    TL::template load<BKV, 4>(ks[0], Kp, D, 0, s, w, lane);
-    TL::template load<BKV, 4>(vs[0], Vp, D, 0, s, w, lane);
+    kvld.issue(ksa, Kp, 0, s, w, lane);
+    kvld.issue(vsa, Vp, 0, s, w, lane);
   }
   wait_dma();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
+    // Opaque to the optimiser: keeps the per-fragment XORs inside the loop
+    // instead of one hoisted address register per fragment.
+    asm volatile("" : "+v"(rf), "+v"(trb));
     if (t + 1 < ntiles) {
-      TL::template load<BKV, 4>(ks[buf ^ 1], Kp, D, (t + 1) * BKV, s, w, lane);
-      TL::template load<BKV, 4>(vs[buf ^ 1], Vp, D, (t + 1) * BKV, s, w, lane);
+      kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
+      kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
     }
     if (wave_active && t < wave_tiles) {
       const int kvb = t * BKV;
@@ -420,8 +542,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
         f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          sacc = mma(TL::frag(ks[buf], 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc);
-          dpacc = mma(TL::frag(vs[buf], 32 * sb + lr, 16 * c + 8 * g), df[c], dpacc);
+          sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
+          dpacc = mma(TL::frag_at(vsa + buf * TB, rf, sb, c), df[c], dpacc);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -441,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
           for (int e = 0; e < 8; ++e) td[e] = dpacc[8 * h2 + e];
           const bf16x8 dsf = pack_frag<bf16>(td);
 #pragma unroll
-          for (int i = 0; i < ND; ++i) dqacc[i] = mma(TL::tr_frag(ks[buf], cc, i, lane), dsf, dqacc[i]);
+          for (int i = 0; i < ND; ++i) dqacc[i] = mma(TL::tr_at(ksa + buf * TB, trb, cc, i), dsf, dqacc[i]);
         }
       }
     }
