@@ -1,6 +1,6 @@
 // bf16 attention kernels (head_dim 64 / 128) whose key/value and query tiles
 // travel global -> LDS by direct LDS loads (global_load_lds_dwordx4: lane l's
-// 16 bytes land at the instruction's LDS base + 16 l), so no register staging
+// 16 bytes land at the instruction's LDS base + 16 l; see dma16_s), so no register staging
 // and no in-register transposes are needed. Tiles are row-major, unpadded,
 // with the 16-byte chunks of row r XOR-permuted by f(r) (see DmaTile) so
 // that both read forms are free of bank conflicts on the 64-bank LDS: a
@@ -58,9 +58,7 @@ struct DmaTile {
       const int r = o / RB, p = (o % RB) >> 4;
       const int gr = min(row0 + r, rlim - 1);
       const bf16* gp = src + (int64_t)gr * ld + ((p ^ f(r)) << 3);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)gp,
-          (__attribute__((address_space(3))) void*)((char*)tile + base), 16, 0, 0);
+      dma16_v(gp, lds_addr((const char*)tile + base));
     }
   }
 
@@ -152,11 +150,7 @@ struct DmaTile {
 #pragma unroll
         for (int m = 0; m < PERW; ++m) {
           const int brow = (w * PERW + m) * RPI;
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(base + brow * ldb +
-                                                              (l ^ (16u * f(brow)))),
-              (__attribute__((address_space(3))) void*)(size_t)(tile + (w * PERW + m) * 1024), 16,
-              0, 0);
+          dma16_s(base + brow * ldb, l ^ (16u * f(brow)), tile + (w * PERW + m) * 1024);
         }
       } else {
         int ln = lane;
@@ -166,22 +160,13 @@ struct DmaTile {
           const int o = (w * PERW + m) * 1024 + 16 * ln;
           const int r = o / RB, p = (o % RB) >> 4;
           const int gr = min(row0 + r, rlim - 1);
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)((const char*)src + gr * ldb +
-                                                              ((p ^ f(r)) << 4)),
-              (__attribute__((address_space(3))) void*)(size_t)(tile + (w * PERW + m) * 1024), 16,
-              0, 0);
+          dma16_v((const char*)src + gr * ldb + ((p ^ f(r)) << 4), tile + (w * PERW + m) * 1024);
         }
       }
     }
   };
 };
 
-// LDS byte address of a shared-memory object.
-template <typename T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
-}
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
 

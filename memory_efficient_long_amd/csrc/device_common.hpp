@@ -128,4 +128,48 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- direct loads
+// global_load_lds_dwordx4: 16 bytes per lane from global memory straight into
+// LDS at M0 + 16 * lane. Issued through inline asm so that the compiler's
+// wait-count pass does not treat every later LDS read as dependent on the
+// load (it cannot tell the tile being filled from the tiles being read, and
+// would wait for all outstanding loads before the first LDS read after it).
+// Callers therefore wait for these loads themselves (s_waitcnt vmcnt) before
+// the barrier that publishes a tile. M0 is saved and restored around the
+// load; one wait state separates the M0 write from the load.
+//
+// dma16_s: wave-uniform 64-bit base (SGPRs) + per-lane 32-bit byte offset.
+// dma16_v: per-lane 64-bit address.
+// lds: wave-uniform LDS byte address of the 64 x 16-byte destination block.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+__device__ __forceinline__ void dma16_v(const void* addr, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(addr)
+      : "memory");
+}
+
+// LDS byte address of a shared-memory object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
+}
+
 }  // namespace bpt

@@ -39,14 +39,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One direct load: 16 bytes per lane from a wave-uniform base plus a per-lane
-// 32-bit byte offset (the scalar-base addressing form, so the only per-load
-// vector work is none), into LDS at the uniform address lds.
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(sbase + voff),
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-
 // K-major tile: R rows x BK bf16.
 template <int R, int BK>
 struct KTile {
@@ -83,7 +75,7 @@ struct KTile {
     __device__ __forceinline__ void issue(char* tile, int k0, int w) const {
       const char* sb = base + (int64_t)k0 * 2;
 #pragma unroll
-      for (int m = 0; m < PERW; ++m) dma16(sb, voff[m], tile + (w * PERW + m) * 1024);
+      for (int m = 0; m < PERW; ++m) dma16_s(sb, voff[m], lds_addr(tile) + (w * PERW + m) * 1024);
     }
   };
   __device__ static __forceinline__ bf16x8 frag(const char* tile, int r, int kc) {
@@ -124,7 +116,7 @@ struct NTile {
     __device__ __forceinline__ void issue(char* tile, int k0, int w) const {
       const char* sb = base + (int64_t)k0 * ld_bytes;
 #pragma unroll
-      for (int m = 0; m < PERW; ++m) dma16(sb, voff[m], tile + (w * PERW + m) * 1024);
+      for (int m = 0; m < PERW; ++m) dma16_s(sb, voff[m], lds_addr(tile) + (w * PERW + m) * 1024);
     }
   };
   // Column n0 + (lane % 32), k = 16 kk + 8 g + {0..7}.
