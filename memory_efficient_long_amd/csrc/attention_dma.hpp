@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   const float sl2 = a.scale_log2;
 
   const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
-  uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
+  const uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
   const typename TL::template Loader<BKV, 4> kvld(D, lane);
   if (ntiles > 0) {
     kvld.issue(ksa, Kp, 0, s, w, lane);
@@ -220,11 +220,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   wait_dma();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    // Opaque to the optimiser: keeps the per-fragment XORs inside the loop
-    // instead of one hoisted address register per fragment.
-    asm volatile("" : "+v"(rf), "+v"(trb));
+  // One key tile per call; the buffer index is a compile-time constant (the
+  // loop below is unrolled by two), so every LDS address is a per-lane base
+  // held in a register plus an immediate offset.
+  auto tile_step = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     if (t + 1 < ntiles) {
       kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
       kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
@@ -262,28 +262,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         m_run = m_new;
       }
-      float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[sb][r], sl2, -m_run));
-          sacc[sb][r] = p;
-          rs += p;
-        }
-      l_run += rs + shfl_xor(rs, 32);
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], sl2, -m_run));
+      // P in bf16 (the B operand of O^T += V^T P^T); the row sum is taken
+      // over the same bf16 values, two per dot-product instruction, so the
+      // normaliser matches what the MFMAs accumulate.
+      bf16x8 pf[4];
+      float rs = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         float tmp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmp[e] = sacc[cc >> 1][8 * (cc & 1) + e];
-        const bf16x8 pf = pack_frag<bf16>(tmp);
-#pragma unroll
-        for (int i = 0; i < ND; ++i) oacc[i] = mma(TL::tr_at(vsa + buf * TB, trb, cc, i), pf, oacc[i]);
+        pf[cc] = pack_frag<bf16>(tmp);
+        rs = row_sum_bf16x8(pf[cc], rs);
       }
+      l_run += rs + shfl_xor(rs, 32);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+          oacc[i] = mma(TL::tr_at(vsa + buf * TB, trb, cc, i), pf[cc], oacc[i]);
     }
     wait_dma();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
   if (wave_active && qrow < s) {

@@ -13,6 +13,8 @@
 // as A and B use the same one.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,6 +129,16 @@ __device__ __forceinline__ void transpose_4xvec(const u32x4 in[4], u32x4 out[4])
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + sum of the eight bf16 values of v: four v_dot2c_f32_bf16 with
+// (1.0, 1.0). Written as inline asm: the builtin's vector operands were
+// observed to be mis-selected (one dword used for all four products).
+__device__ __forceinline__ float row_sum_bf16x8(const bf16x8& v, float acc) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(u[k]));
+  return acc;
+}
 
 // ---------------------------------------------------------------- direct loads
 // global_load_lds_dwordx4: 16 bytes per lane from global memory straight into
