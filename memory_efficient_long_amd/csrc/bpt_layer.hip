@@ -94,7 +94,7 @@ struct TimedLaunch {
 };
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
-constexpr int kNormWaves = 256;    // waves of the norm backward (partial rows)
+constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -332,10 +332,15 @@ bpt_status norm_fwd(hipStream_t st, const Plan& p, const Tin* x, int64_t ldx, co
   return check_launch("norm_fwd");
 }
 
+// Norm backward over `rows` rows. The gain / shift gradients go to per-wave
+// partial rows (part_g / part_b, kNormWaves x h): with `stage` == 0 they are
+// written, 1 accumulated (several calls over row blocks), and with `finish`
+// reduced into dg / db (+=).
 template <typename T, typename Tin, typename Tres>
 bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz, const Tin* xin,
                     int64_t ldx, const T* g, const Tres* res, int64_t ldr, float* out_f, T* out_t,
-                    int64_t ldo, int64_t rows, float* dg, float* db, float* part_g, float* part_b) {
+                    int64_t ldo, int64_t rows, float* dg, float* db, float* part_g, float* part_b,
+                    int stage, bool finish, int* nparts) {
   if (rows == 0) return BPT_OK;
   const int nch = (int)((p.h / 8 + 63) / 64);
   const int kind = p.norm == BPT_LAYERNORM ? NORM_LAYER : NORM_RMS;
@@ -346,30 +351,42 @@ bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz
   TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
 #define NB(NC) hipLaunchKernelGGL((norm_bwd_kernel<T, Tin, Tres, NC>), grid, blk, 0, st, dz, lddz, xin, \
                                   ldx, g, res, ldr, out_f, out_t, ldo, pg, pb, (int)rows, (int)p.h,  \
-                                  kind, p.eps)
+                                  kind, p.eps, stage)
   if (nch <= 1) NB(1); else if (nch <= 2) NB(2); else if (nch <= 4) NB(4);
   else if (nch <= 8) NB(8); else if (nch <= 16) NB(16); else if (nch <= 32) NB(32);
   else return fail(BPT_EUNSUPPORTED, "hidden too large for norm kernel");
 #undef NB
   BPT_TRY(check_launch("norm_bwd"));
-  const int P = nblk * 4;
+  // The first call of a series writes the most partial rows (it has the most
+  // rows); later calls accumulate into a prefix of them.
+  if (stage == 0) *nparts = nblk * 4;
+  if (!finish) return BPT_OK;
+  const int P = *nparts;
   const dim3 g2((unsigned)((p.h + 63) / 64));
   if (dg) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pg, P, (int)p.h, dg, 1);
   if (db) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pb, P, (int)p.h, db, 1);
   return check_launch("norm_bwd reduce");
 }
 
-// out[col] += sum over rows of X[:, col]
+// out[col] += sum over rows of X[:, col]. A series of calls over row blocks
+// can share the partial rows: `stage` 0 writes them, 1 accumulates; `finish`
+// reduces them into out. The first call of a series must have the most rows.
 template <typename Tin>
 bpt_status colsum(hipStream_t st, const Tin* X, int64_t ldx, int64_t rows, int64_t N, float* part,
-                  float* out) {
-  if (!out || rows == 0 || N == 0) return BPT_OK;
-  const int P = (int)std::min<int64_t>(kColsumParts, rows);
+                  float* out, int stage = 0, bool finish = true, int* nparts = nullptr) {
+  if (!out || N == 0) return BPT_OK;
+  int P = (int)std::min<int64_t>(kColsumParts, rows);
   TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
-  hipLaunchKernelGGL(colsum_partial_kernel<Tin>, dim3((unsigned)((N + 63) / 64), P), dim3(256), 0,
-                     st, X, ldx, (int)rows, (int)N, part);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
-                     part, P, (int)N, out, 1);
+  if (rows > 0)
+    hipLaunchKernelGGL(colsum_partial_kernel<Tin>, dim3((unsigned)((N + 63) / 64), P), dim3(256), 0,
+                       st, X, ldx, (int)rows, (int)N, part, stage);
+  if (nparts) {
+    if (stage == 0) *nparts = P;
+    P = *nparts;
+  }
+  if (finish && P > 0)
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
+                       part, P, (int)N, out, 1);
   return check_launch("colsum");
 }
 
@@ -564,6 +581,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
 
     // ---- per query block: FFN, Norm2 and O-projection backward
+    int np_db1 = 0, np_n2 = 0;
     for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
       const T* Oi = Ob + r0 * HD;
       const T* dyi = dyb + r0 * p.h;
@@ -583,7 +601,6 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
         EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
         BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyi, p.h, p.f, p.h, p.cq, e, "dW2")));
       }
-      BPT_TRY(colsum<T>(st, dyi, p.h, p.cq, p.h, w.part, db2));
       if (swiglu) {
         EpiSwiGrad<T> e{w.da, w.dup, w.a, w.up, p.f};
         BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du (swiglu)")));
@@ -599,7 +616,11 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
         EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
         BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, p.cq, e, "dW3")));
       }
-      BPT_TRY(colsum<T>(st, w.da, p.f, p.cq, p.f, w.part, db1));
+      // Bias and norm-parameter gradients of the block: partial column sums
+      // accumulate over the blocks and are reduced after the last one.
+      const int first = r0 == 0 ? 0 : 1;
+      const bool last = r0 + p.cq >= p.s;
+      BPT_TRY(colsum<T>(st, w.da, p.f, p.cq, p.f, w.part, db1, first, last, &np_db1));
       {
         EpiOut<T, float> e{w.dz, p.h, nullptr, 1.f, 0};
         BPT_TRY((gemm<T, true, true>(st, w.da, p.f, w1, p.f, p.cq, p.h, p.f, e, "dz")));
@@ -610,17 +631,22 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       }
       float* dh_rows = w.dh + r0 * p.h;
       BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, w.h1, p.h, g2, dyi, p.h, dh_rows, w.dh_t,
-                                     p.h, p.cq, dg2, dsh2, w.npart_g, w.npart_b)));
+                                     p.h, p.cq, dg2, dsh2, w.npart_g, w.npart_b, first, last,
+                                     &np_n2)));
       if (dwo) {
         EpiOut<T, float> e{dwo, p.h, nullptr, 1.f, 1};
         BPT_TRY((gemm<T, false, false>(st, Oi, HD, w.dh_t, p.h, HD, p.h, p.cq, e, "dWo")));
       }
-      BPT_TRY(colsum<float>(st, dh_rows, p.h, p.cq, p.h, w.part, dbo));
       {
         EpiOut<T, T> e{w.dO + r0 * HD, HD, nullptr, 1.f, 0};
         BPT_TRY((gemm<T, true, true>(st, w.dh_t, p.h, wo, p.h, p.cq, HD, p.h, e, "dO")));
       }
     }
+
+    // Output-bias gradients over the whole sequence: db_2 = sum of dy rows,
+    // db_o = sum of the rows of dh (the gradient at the attention residual).
+    BPT_TRY(colsum<T>(st, dyb, p.h, p.s, p.h, w.part, db2));
+    BPT_TRY(colsum<float>(st, w.dh, p.h, p.s, p.h, w.part, dbo));
 
     // ---- attention backward per head chunk
     {
@@ -654,8 +680,9 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       }
     }
     // ---- Norm1 backward + residual: dx = dh + Norm1'(dxn)
+    int np_n1 = 0;
     BPT_TRY((norm_bwd<T, T, float>(st, p, w.dxn, p.h, xb, p.h, g1, w.dh, p.h, nullptr, dxb, p.h,
-                                   p.s, dg1, dsh1, w.npart_g, w.npart_b)));
+                                   p.s, dg1, dsh1, w.npart_g, w.npart_b, 0, true, &np_n1)));
   }
   return BPT_OK;
 }

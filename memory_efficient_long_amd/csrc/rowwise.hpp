@@ -97,7 +97,8 @@ template <typename T, typename Tin, typename Tres, int NCH>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const float* __restrict__ dz, int64_t lddz, const Tin* __restrict__ xin, int64_t ldx,
     const T* __restrict__ gamma, const Tres* __restrict__ res, int64_t ldr, float* out_f,
-    T* out_t, int64_t ldo, float* part_g, float* part_b, int rows, int h, int kind, float eps) {
+    T* out_t, int64_t ldo, float* part_g, float* part_b, int rows, int h, int kind, float eps,
+    int accumulate_part) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
@@ -172,6 +173,19 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
+      if (accumulate_part) {  // running partials over several calls
+        float og[8], ob[8];
+        if (part_g) {
+          load8(part_g + (int64_t)wave * h + 8 * c, og);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pg[i][e] += og[e];
+        }
+        if (part_b) {
+          load8(part_b + (int64_t)wave * h + 8 * c, ob);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[i][e] += ob[e];
+        }
+      }
       if (part_g) store8(part_g + (int64_t)wave * h + 8 * c, pg[i]);
       if (part_b) store8(part_b + (int64_t)wave * h + 8 * c, pb[i]);
     }
@@ -182,7 +196,8 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
 // (64 columns x 4 row lanes); part[blockIdx.y, col] = sum over the block's rows.
 template <typename Tin>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restrict__ X, int64_t ldx,
-                                                             int rows, int N, float* part) {
+                                                             int rows, int N, float* part,
+                                                             int accumulate) {
   __shared__ float red[4][64];
   const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + cl;
@@ -193,8 +208,11 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restri
     for (int r = r0 + rl; r < r1; r += 4) acc += to_f32(X[(int64_t)r * ldx + col]);
   red[rl][cl] = acc;
   __syncthreads();
-  if (rl == 0 && col < N)
-    part[(int64_t)blockIdx.y * N + col] = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+  if (rl == 0 && col < N) {
+    const float v = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+    float* o = part + (int64_t)blockIdx.y * N + col;
+    *o = accumulate ? *o + v : v;
+  }
 }
 
 // Stage 2: out[col] (+)= sum_p part[p, col]; block = 64 columns x 4 partial
