@@ -110,9 +110,15 @@ struct DmaTile {
     return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(tile + 32 * blk * RB +
                                                                        (rf ^ (32u * c)));
   }
+  // SPLIT: the second address as its own constant + (tr ^ (64 i + 32)) (tile
+  // + 16 cc RB is a multiple of 256, so this equals the first address ^ 32,
+  // plus 8 rows) -- one XOR per read with no dependence on the first address;
+  // otherwise derived from the first address.
+  template <bool SPLIT = true>
   __device__ static __forceinline__ bf16x8 tr_at(uint32_t tile, uint32_t tr, int cc, int i) {
     const uint32_t a0 = tile + 16 * cc * RB + (tr ^ (64u * i));
-    const uint32_t a1 = (a0 ^ 32u) + 8 * RB;
+    const uint32_t a1 = SPLIT ? tile + 16 * cc * RB + 8 * RB + (tr ^ (64u * i + 32u))
+                              : (a0 ^ 32u) + 8 * RB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(size_t)a0);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
         for (int i = 0; i < ND; ++i)
-          oacc[i] = mma(TL::tr_at(vsa + buf * TB, trb, cc, i), pf[cc], oacc[i]);
+          oacc[i] = mma(TL::template tr_at<false>(vsa + buf * TB, trb, cc, i), pf[cc], oacc[i]);
     }
     wait_dma();
     __syncthreads();
@@ -383,10 +389,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   wait_dma();
   __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
+  // One query tile per call with a compile-time buffer index (the loop is
+  // unrolled by two): every LDS address is a constant plus a per-lane base
+  // XOR an immediate. The bases are made opaque per step so that the XORs
+  // stay next to their reads instead of occupying a register each.
+  auto q_step = [&](int step, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int q0 = (qt0 + step % per_head) * BQ;
-    const int buf = step & 1;
-    asm volatile("" : "+v"(rf), "+v"(trb));  // see the forward kernel
+    asm volatile("" : "+v"(rf), "+v"(trb));
     if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
     const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
 #pragma unroll
@@ -442,6 +452,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     if (step + 1 < nsteps) store_stats(buf ^ 1);
     wait_dma();
     __syncthreads();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    q_step(step, std::integral_constant<int, 0>());
+    if (step + 1 < nsteps) q_step(step + 1, std::integral_constant<int, 1>());
   }
 
 #pragma unroll
@@ -518,10 +532,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   wait_dma();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    // Opaque to the optimiser: keeps the per-fragment XORs inside the loop
-    // instead of one hoisted address register per fragment.
+  // One key tile per call with a compile-time buffer index (unrolled by two):
+  // LDS addresses are constants plus a per-lane base XOR an immediate; the
+  // bases are opaque per tile so the XORs stay next to their reads rather
+  // than taking a register each.
+  auto tile_step = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     asm volatile("" : "+v"(rf), "+v"(trb));
     if (t + 1 < ntiles) {
       kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
@@ -562,6 +578,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
     }
     wait_dma();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
   if (wave_active && qrow < s) {
