@@ -39,21 +39,28 @@ __device__ __forceinline__ float sigmoidf_(float a) { return 1.f / (1.f + expf(-
 enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
 
 // ----------------------------------------------------------------- epilogues
-// Each epilogue is called once per in-bounds output element with the fp32
-// accumulator value v (and, when kPair, the value of column n ^ 1 in the same
-// row, used by the RoPE rotation).
+// Each epilogue is applied to the in-bounds output elements of one 32 x 32
+// accumulator block in two phases: pre(m, n) gathers the element's other
+// inputs (bias, residual, previous value, ...) for all 16 rows of a lane
+// first, then apply(m, n, v, vp, pre) computes and stores. Gathering first
+// matters on this GPU: vector-memory loads and stores share one in-order
+// counter, so a load issued after stores cannot be waited for without also
+// waiting for the stores. v is the fp32 accumulator value; vp, when kPair,
+// the value of column n ^ 1 in the same row (used by the RoPE rotation).
 
 // out = alpha * v (+ bias[n]) (+ out if accumulate)
 template <typename T, typename OutT>
 struct EpiOut {
   OutT* out; int64_t ldo; const T* bias; float alpha; int accumulate;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
-    float r = alpha * v;
-    if (bias) r += to_f32(bias[n]);
-    OutT* p = out + (int64_t)m * ldo + n;
-    if (accumulate) r += to_f32(*p);
-    *p = from_f32<OutT>(r);
+  struct Pre { float add; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    float add = bias ? to_f32(bias[n]) : 0.f;
+    if (accumulate) add += to_f32(out[(int64_t)m * ldo + n]);
+    return {add};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+    out[(int64_t)m * ldo + n] = from_f32<OutT>(fmaf(alpha, v, p.add));
   }
 };
 
@@ -63,13 +70,20 @@ template <typename T>
 struct EpiQKV {
   T* out; int64_t head_stride; int D; const T* bias; const float2* rope; int row0;
   static constexpr bool kPair = true;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float vp) const {
-    if (bias) { v += to_f32(bias[n]); vp += to_f32(bias[n ^ 1]); }
-    const int head = n / D, dd = n - head * D;
+  struct Pre { float b, bp; float2 cs; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    Pre p{0.f, 0.f, {1.f, 0.f}};
+    if (bias) { p.b = to_f32(bias[n]); p.bp = to_f32(bias[n ^ 1]); }
     if (rope) {
-      float2 cs = rope[(int64_t)(row0 + m) * (D / 2) + (dd >> 1)];
-      v = (dd & 1) ? (vp * cs.y + v * cs.x) : (v * cs.x - vp * cs.y);
+      const int dd = n % D;
+      p.cs = rope[(int64_t)(row0 + m) * (D / 2) + (dd >> 1)];
     }
+    return p;
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Pre& p) const {
+    v += p.b; vp += p.bp;
+    const int head = n / D, dd = n - head * D;
+    if (rope) v = (dd & 1) ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
     out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
   }
 };
@@ -79,10 +93,12 @@ template <typename T, typename ResT, typename OutT>
 struct EpiResid {
   OutT* out; int64_t ldo; const ResT* res; int64_t ldr; const T* bias;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
-    if (bias) v += to_f32(bias[n]);
-    v += to_f32(res[(int64_t)m * ldr + n]);
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(v);
+  struct Pre { float add; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    return {(bias ? to_f32(bias[n]) : 0.f) + to_f32(res[(int64_t)m * ldr + n])};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+    out[(int64_t)m * ldo + n] = from_f32<OutT>(v + p.add);
   }
 };
 
@@ -91,8 +107,10 @@ template <typename T>
 struct EpiAct {
   T* u; T* a_keep; int64_t ldo; const T* bias; int act;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
-    if (bias) v += to_f32(bias[n]);
+  struct Pre { float b; };
+  __device__ __forceinline__ Pre pre(int, int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+    v += p.b;
     const int64_t i = (int64_t)m * ldo + n;
     if (a_keep) a_keep[i] = from_f32<T>(v);
     u[i] = from_f32<T>(act == ACT_RELU ? act_relu(v) : act_gelu(v));
@@ -104,11 +122,14 @@ template <typename T>
 struct EpiSwiUp {
   T* u; T* up_keep; const T* gate; int64_t ldo;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+  struct Pre { float g; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    return {to_f32(gate[(int64_t)m * ldo + n])};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
     const int64_t i = (int64_t)m * ldo + n;
     if (up_keep) up_keep[i] = from_f32<T>(v);
-    float g = to_f32(gate[i]);
-    u[i] = from_f32<T>(g * sigmoidf_(g) * v);
+    u[i] = from_f32<T>(p.g * sigmoidf_(p.g) * v);
   }
 };
 
@@ -117,11 +138,13 @@ template <typename T>
 struct EpiActGrad {
   T* da; const T* a; int64_t ldo; int act;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
-    const int64_t i = (int64_t)m * ldo + n;
-    float x = to_f32(a[i]);
-    float gr = act == ACT_RELU ? (x > 0.f ? 1.f : 0.f) : act_gelu_grad(x);
-    da[i] = from_f32<T>(v * gr);
+  struct Pre { float x; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    return {to_f32(a[(int64_t)m * ldo + n])};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+    const float gr = act == ACT_RELU ? (p.x > 0.f ? 1.f : 0.f) : act_gelu_grad(p.x);
+    da[(int64_t)m * ldo + n] = from_f32<T>(v * gr);
   }
 };
 
@@ -131,14 +154,39 @@ template <typename T>
 struct EpiSwiGrad {
   T* dgate; T* dup; const T* gate; const T* up; int64_t ldo;
   static constexpr bool kPair = false;
-  __device__ __forceinline__ void operator()(int m, int n, float v, float) const {
+  struct Pre { float g, u; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
     const int64_t i = (int64_t)m * ldo + n;
-    float g = to_f32(gate[i]), u = to_f32(up[i]);
-    float sg = sigmoidf_(g);
-    dgate[i] = from_f32<T>(v * u * sg * (1.f + g * (1.f - sg)));
-    dup[i] = from_f32<T>(v * g * sg);
+    return {to_f32(gate[i]), to_f32(up[i])};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+    const int64_t i = (int64_t)m * ldo + n;
+    const float sg = sigmoidf_(p.g);
+    dgate[i] = from_f32<T>(v * p.u * sg * (1.f + p.g * (1.f - sg)));
+    dup[i] = from_f32<T>(v * p.g * sg);
   }
 };
+
+// Epilogue of one 32 x 32 accumulator block (rows m0 + acc_row(r, g), column
+// col of this lane): gather, then apply.
+template <bool EVEN, class Epi>
+__device__ __forceinline__ void epilogue_block(const Epi& epi, const f32x16& acc, int m0, int col,
+                                               int g, int M, int N) {
+  typename Epi::Pre pre[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + acc_row(r, g);
+    if (EVEN || (row < M && col < N)) pre[r] = epi.pre(row, col);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + acc_row(r, g);
+    const float v = acc[r];
+    float vp = 0.f;
+    if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
+    if (EVEN || (row < M && col < N)) epi.apply(row, col, v, vp, pre[r]);
+  }
+}
 
 // ----------------------------------------------------------------- tile loaders
 // Loads one operand tile (R rows x BK reduction) into registers and stores it
@@ -301,17 +349,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int6
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn0 + 32 * j + lr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + 32 * i + acc_row(r, g);
-        float v = acc[i][j][r];
-        float vp = 0.f;
-        if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
-        if (EVEN || (row < M && col < N)) epi(row, col, v, vp);
-      }
-    }
+    for (int j = 0; j < FN; ++j)
+      epilogue_block<EVEN>(epi, acc[i][j], m0 + wm0 + 32 * i, n0 + wn0 + 32 * j + lr, g, M, N);
 }
 
 }  // namespace bpt

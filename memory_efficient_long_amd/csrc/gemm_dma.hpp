@@ -251,17 +251,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn0 + 32 * j + lr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + 32 * i + acc_row(r, g);
-        float v = acc[i][j][r];
-        float vp = 0.f;
-        if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
-        if (row < M && col < N) epi(row, col, v, vp);
-      }
-    }
+    for (int j = 0; j < FN; ++j)
+      epilogue_block<false>(epi, acc[i][j], m0 + wm0 + 32 * i, n0 + wn0 + 32 * j + lr, g, M, N);
 }
 
 }  // namespace bpt
