@@ -179,7 +179,7 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
   w.q = c.take<T>(p.U * p.s * p.D);
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
-  w.h1 = c.take<float>(p.cq * p.h);
+  w.h1 = c.take<float>(p.s * p.h);  // x + attention output projection, whole sequence
   w.z = c.take<T>(p.cq * p.h);
   w.u = c.take<T>(p.cq * p.f);
   w.gate = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
@@ -207,7 +207,7 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
   w.dqkv = c.take<T>(p.s * p.chunk_cols);
-  w.h1 = c.take<float>(p.cq * p.h);
+  w.h1 = c.take<float>(p.s * p.h);  // recomputed x + O W_o + b_o, whole sequence
   w.z = c.take<T>(p.cq * p.h);
   w.a = c.take<T>(p.cq * p.f);
   w.u = c.take<T>(p.cq * p.f);
@@ -215,7 +215,7 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.da = c.take<T>(p.cq * p.f);
   w.dup = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
   w.dz = c.take<float>(p.cq * p.h);
-  w.dh_t = c.take<T>(p.cq * p.h);
+  w.dh_t = c.take<T>(p.s * p.h);  // dh in the storage type, whole sequence
   const int64_t maxn = std::max<int64_t>(std::max(p.h, p.f), std::max(p.chunk_cols, HD));
   w.part = c.take<float>(kColsumParts * maxn);
   w.npart_g = c.take<float>(kNormWaves * p.h);
@@ -512,11 +512,15 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
       BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s));
     }
+    // Output projection + residual for the whole sequence in one GEMM (it is
+    // position-wise; only the FFN needs the per-block scratch).
+    {
+      EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
+      BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection")));
+    }
     for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
-      const T* Oi = Ob + r0 * HD;
-      EpiResid<T, T, float> eo{w.h1, p.h, xb + r0 * p.h, p.h, bo};
-      BPT_TRY((gemm<T, true, false>(st, Oi, HD, wo, p.h, p.cq, p.h, HD, eo, "o projection")));
-      BPT_TRY((norm_fwd<T, float, T>(st, p, w.h1, p.h, g2, sh2, w.z, p.h, p.cq)));
+      const float* h1i = w.h1 + r0 * p.h;
+      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, w.z, p.h, p.cq)));
       if (p.ffn == BPT_SWIGLU) {
         EpiOut<T, T> eg{w.gate, p.f, b1, 1.f, 0};
         BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate")));
@@ -526,7 +530,7 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
         EpiAct<T> ea{w.u, nullptr, p.f, b1, act};
         BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1")));
       }
-      EpiResid<T, float, T> ey{yb + r0 * p.h, p.h, w.h1, p.h, b2};
+      EpiResid<T, float, T> ey{yb + r0 * p.h, p.h, h1i, p.h, b2};
       BPT_TRY((gemm<T, true, false>(st, w.u, p.f, w2, p.h, p.cq, p.h, p.f, ey, "ffn fc2")));
     }
   }
@@ -580,14 +584,17 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     const float* Lb = LSE + bi * p.H * p.s;
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
 
-    // ---- per query block: FFN, Norm2 and O-projection backward
+    // ---- h1 = x + O W_o + b_o recomputed for the whole sequence
+    {
+      EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
+      BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection (re)")));
+    }
+    // ---- per query block: FFN and Norm2 backward
     int np_db1 = 0, np_n2 = 0;
     for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
-      const T* Oi = Ob + r0 * HD;
       const T* dyi = dyb + r0 * p.h;
-      EpiResid<T, T, float> eo{w.h1, p.h, xb + r0 * p.h, p.h, bo};
-      BPT_TRY((gemm<T, true, false>(st, Oi, HD, wo, p.h, p.cq, p.h, HD, eo, "o projection (re)")));
-      BPT_TRY((norm_fwd<T, float, T>(st, p, w.h1, p.h, g2, sh2, w.z, p.h, p.cq)));
+      const float* h1i = w.h1 + r0 * p.h;
+      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, w.z, p.h, p.cq)));
       if (swiglu) {
         EpiOut<T, T> eg{w.a, p.f, b1, 1.f, 0};   // w.a holds the gate pre-activation
         BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate (re)")));
@@ -630,17 +637,19 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
         }
       }
       float* dh_rows = w.dh + r0 * p.h;
-      BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, w.h1, p.h, g2, dyi, p.h, dh_rows, w.dh_t,
-                                     p.h, p.cq, dg2, dsh2, w.npart_g, w.npart_b, first, last,
-                                     &np_n2)));
-      if (dwo) {
-        EpiOut<T, float> e{dwo, p.h, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, Oi, HD, w.dh_t, p.h, HD, p.h, p.cq, e, "dWo")));
-      }
-      {
-        EpiOut<T, T> e{w.dO + r0 * HD, HD, nullptr, 1.f, 0};
-        BPT_TRY((gemm<T, true, true>(st, w.dh_t, p.h, wo, p.h, p.cq, HD, p.h, e, "dO")));
-      }
+      BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, h1i, p.h, g2, dyi, p.h, dh_rows,
+                                     w.dh_t + r0 * p.h, p.h, p.cq, dg2, dsh2, w.npart_g,
+                                     w.npart_b, first, last, &np_n2)));
+    }
+    // ---- O-projection backward over the whole sequence: dW_o += O^T dh,
+    // dO = dh W_o^T.
+    if (dwo) {
+      EpiOut<T, float> e{dwo, p.h, nullptr, 1.f, 1};
+      BPT_TRY((gemm<T, false, false>(st, Ob, HD, w.dh_t, p.h, HD, p.h, p.s, e, "dWo")));
+    }
+    {
+      EpiOut<T, T> e{w.dO, HD, nullptr, 1.f, 0};
+      BPT_TRY((gemm<T, true, true>(st, w.dh_t, p.h, wo, p.h, p.s, HD, p.h, e, "dO")));
     }
 
     // Output-bias gradients over the whole sequence: db_2 = sum of dy rows,
