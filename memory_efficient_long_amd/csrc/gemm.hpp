@@ -26,15 +26,36 @@ namespace bpt {
 
 // ----------------------------------------------------------------- activations
 __device__ __forceinline__ float act_relu(float a) { return a > 0.f ? a : 0.f; }
+// erf(x) for x >= 0 together with exp(-x^2), by the rational approximation
+// of Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2), t = 1 / (1 + p x), absolute
+// error <= 1.5e-7 -- far below the bf16 rounding of the GEMM outputs it
+// feeds, at a fraction of the cost of a full-precision erff.
+__device__ __forceinline__ float erf_as(float x, float& ex2) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                       -0.284496736f),
+               0.254829592f);
+  ex2 = fast_exp2(-x * x * 1.4426950408889634f);
+  return 1.f - poly * ex2;
+}
+// GELU with the exact (erf) form: 0.5 a (1 + erf(a / sqrt 2)).
 __device__ __forceinline__ float act_gelu(float a) {
-  return 0.5f * a * (1.f + erff(a * 0.70710678118654752f));
+  float ex2;
+  const float e = erf_as(fabsf(a) * 0.70710678118654752f, ex2);
+  return 0.5f * a * (1.f + copysignf(e, a));
 }
+// d GELU / da = Phi(a) + a phi(a); exp(-(a / sqrt 2)^2) is phi's exponential.
 __device__ __forceinline__ float act_gelu_grad(float a) {
-  float cdf = 0.5f * (1.f + erff(a * 0.70710678118654752f));
-  float pdf = 0.39894228040143268f * expf(-0.5f * a * a);
-  return cdf + a * pdf;
+  float ex2;
+  const float e = erf_as(fabsf(a) * 0.70710678118654752f, ex2);
+  return 0.5f * (1.f + copysignf(e, a)) + a * 0.39894228040143268f * ex2;
 }
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.f / (1.f + expf(-a)); }
+// 1 / (1 + e^-a) with the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float sigmoidf_(float a) {
+  return __builtin_amdgcn_rcpf(1.f + fast_exp2(-a * 1.4426950408889634f));
+}
 
 enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
 
