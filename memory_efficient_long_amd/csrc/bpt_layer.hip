@@ -473,6 +473,13 @@ bpt_status qkv_chunk(hipStream_t st, const Plan& p, const T* xn, const T* wqkv, 
   const int64_t hq0 = c * p.U, hk0 = hq0 / p.G;
   const int64_t cols[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
   const int64_t widths[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};
+  if (p.U == p.H) {  // all heads in one chunk: one GEMM over the packed Q|K|V columns
+    EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv, rope, (int)(p.H * p.D),
+                 (int)((p.H + p.Hkv) * p.D)};
+    BPT_TRY((gemm<T, true, false>(st, xn, p.h, wqkv, p.qkv_cols, p.s, p.qkv_cols, p.h, e,
+                                  "qkv projection")));
+    return BPT_OK;
+  }
   T* outs[3] = {q, k, v};
   for (int part = 0; part < 3; ++part) {
     EpiQKV<T> e{outs[part], p.s * p.D, (int)p.D, bqkv ? bqkv + cols[part] : nullptr,
@@ -674,6 +681,20 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       const int64_t segc[3] = {0, p.U * p.D, (p.U + p.nkvc) * p.D};
       const int64_t wcol[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
       const int64_t wid[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};
+      if (p.U == p.H) {
+        // One chunk: dQ|dK|dV are the packed QKV columns in order, so the
+        // weight gradient, bias gradient and dxn are single GEMMs / sums.
+        if (dwqkv) {
+          EpiOut<T, float> e{dwqkv, p.qkv_cols, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, w.dqkv, p.chunk_cols, p.h, p.qkv_cols,
+                                         p.s, e, "dWqkv")));
+        }
+        BPT_TRY(colsum<T>(st, w.dqkv, p.chunk_cols, p.s, p.qkv_cols, w.part, dbqkv));
+        EpiOut<T, float> e{w.dxn, p.h, nullptr, 1.f, 0};
+        BPT_TRY((gemm<T, true, true>(st, w.dqkv, p.chunk_cols, wqkv, p.qkv_cols, p.s, p.h,
+                                     p.qkv_cols, e, "dxn")));
+        continue;
+      }
       for (int seg = 0; seg < 3; ++seg) {
         const T* dseg = w.dqkv + segc[seg];
         if (dwqkv) {

@@ -109,6 +109,30 @@ struct EpiQKV {
   }
 };
 
+// Q, K and V projections of all heads in one GEMM (columns [0, c1) -> q,
+// [c1, c2) -> k, [c2, N) -> v; c1, c2 multiples of D): + bias, RoPE on the
+// q and k columns, scattered to head-major [heads, s, D] buffers.
+template <typename T>
+struct EpiQKV3 {
+  T* q; T* k; T* v; int64_t head_stride; int D; const T* bias; const float2* rope; int c1, c2;
+  static constexpr bool kPair = true;
+  struct Pre { float b, bp; float2 cs; };
+  __device__ __forceinline__ Pre pre(int m, int n) const {
+    Pre p{0.f, 0.f, {1.f, 0.f}};
+    if (bias) { p.b = to_f32(bias[n]); p.bp = to_f32(bias[n ^ 1]); }
+    if (rope && n < c2) p.cs = rope[(int64_t)m * (D / 2) + ((n % D) >> 1)];
+    return p;
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Pre& p) const {
+    v += p.b; vp += p.bp;
+    T* out = n < c1 ? q : (n < c2 ? k : this->v);
+    const int nn = n < c1 ? n : (n < c2 ? n - c1 : n - c2);
+    const int head = nn / D, dd = nn - head * D;
+    if (rope && n < c2) v = (dd & 1) ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
+    out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
+  }
+};
+
 // out = v + bias[n] + res[m, n]
 template <typename T, typename ResT, typename OutT>
 struct EpiResid {
