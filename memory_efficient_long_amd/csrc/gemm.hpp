@@ -60,28 +60,31 @@ __device__ __forceinline__ float sigmoidf_(float a) {
 enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
 
 // ----------------------------------------------------------------- epilogues
-// Each epilogue is applied to the in-bounds output elements of one 32 x 32
-// accumulator block in two phases: pre(m, n) gathers the element's other
-// inputs (bias, residual, previous value, ...) for all 16 rows of a lane
-// first, then apply(m, n, v, vp, pre) computes and stores. Gathering first
-// matters on this GPU: vector-memory loads and stores share one in-order
-// counter, so a load issued after stores cannot be waited for without also
-// waiting for the stores. v is the fp32 accumulator value; vp, when kPair,
-// the value of column n ^ 1 in the same row (used by the RoPE rotation).
+// Each epilogue is applied to one 32 x 32 accumulator block of a lane (one
+// column, 16 rows) in three steps: col(n) loads what depends on the column
+// only (a bias), pre(m, n, col) gathers each element's other inputs
+// (residual, previous value, ...) for all 16 rows, then apply(...) computes
+// and stores. Gathering first, unconditionally from clamped indices, matters
+// on this GPU: vector-memory loads and stores share one in-order counter, so
+// a load issued after stores -- or inside its own branch -- cannot be waited
+// for without also waiting for everything before it. v is the fp32
+// accumulator value; vp, when kPair, the value of column n ^ 1 in the same
+// row (used by the RoPE rotation).
 
 // out = alpha * v (+ bias[n]) (+ out if accumulate)
 template <typename T, typename OutT>
 struct EpiOut {
   OutT* out; int64_t ldo; const T* bias; float alpha; int accumulate;
   static constexpr bool kPair = false;
-  struct Pre { float add; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
-    float add = bias ? to_f32(bias[n]) : 0.f;
-    if (accumulate) add += to_f32(out[(int64_t)m * ldo + n]);
-    return {add};
+  struct Col { float b; };
+  struct Pre { float o; };
+  __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
+    return {accumulate ? to_f32(out[(int64_t)m * ldo + n]) : 0.f};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(fmaf(alpha, v, p.add));
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
+                                        const Pre& p) const {
+    out[(int64_t)m * ldo + n] = from_f32<OutT>(fmaf(alpha, v, c.b + p.o));
   }
 };
 
@@ -91,18 +94,18 @@ template <typename T>
 struct EpiQKV {
   T* out; int64_t head_stride; int D; const T* bias; const float2* rope; int row0;
   static constexpr bool kPair = true;
-  struct Pre { float b, bp; float2 cs; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
-    Pre p{0.f, 0.f, {1.f, 0.f}};
-    if (bias) { p.b = to_f32(bias[n]); p.bp = to_f32(bias[n ^ 1]); }
-    if (rope) {
-      const int dd = n % D;
-      p.cs = rope[(int64_t)(row0 + m) * (D / 2) + (dd >> 1)];
-    }
-    return p;
+  struct Col { float b, bp; };
+  struct Pre { float2 cs; };
+  __device__ __forceinline__ Col col(int n) const {
+    return bias ? Col{to_f32(bias[n]), to_f32(bias[n ^ 1])} : Col{0.f, 0.f};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Pre& p) const {
-    v += p.b; vp += p.bp;
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
+    if (!rope) return {{1.f, 0.f}};
+    return {rope[(int64_t)(row0 + m) * (D / 2) + ((n % D) >> 1)]};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Col& c,
+                                        const Pre& p) const {
+    v += c.b; vp += c.bp;
     const int head = n / D, dd = n - head * D;
     if (rope) v = (dd & 1) ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
     out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
@@ -116,15 +119,18 @@ template <typename T>
 struct EpiQKV3 {
   T* q; T* k; T* v; int64_t head_stride; int D; const T* bias; const float2* rope; int c1, c2;
   static constexpr bool kPair = true;
-  struct Pre { float b, bp; float2 cs; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
-    Pre p{0.f, 0.f, {1.f, 0.f}};
-    if (bias) { p.b = to_f32(bias[n]); p.bp = to_f32(bias[n ^ 1]); }
-    if (rope && n < c2) p.cs = rope[(int64_t)m * (D / 2) + ((n % D) >> 1)];
-    return p;
+  struct Col { float b, bp; };
+  struct Pre { float2 cs; };
+  __device__ __forceinline__ Col col(int n) const {
+    return bias ? Col{to_f32(bias[n]), to_f32(bias[n ^ 1])} : Col{0.f, 0.f};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Pre& p) const {
-    v += p.b; vp += p.bp;
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
+    if (!rope || n >= c2) return {{1.f, 0.f}};
+    return {rope[(int64_t)m * (D / 2) + ((n % D) >> 1)]};
+  }
+  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Col& c,
+                                        const Pre& p) const {
+    v += c.b; vp += c.bp;
     T* out = n < c1 ? q : (n < c2 ? k : this->v);
     const int nn = n < c1 ? n : (n < c2 ? n - c1 : n - c2);
     const int head = nn / D, dd = nn - head * D;
@@ -138,12 +144,15 @@ template <typename T, typename ResT, typename OutT>
 struct EpiResid {
   OutT* out; int64_t ldo; const ResT* res; int64_t ldr; const T* bias;
   static constexpr bool kPair = false;
-  struct Pre { float add; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
-    return {(bias ? to_f32(bias[n]) : 0.f) + to_f32(res[(int64_t)m * ldr + n])};
+  struct Col { float b; };
+  struct Pre { float r; };
+  __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
+    return {to_f32(res[(int64_t)m * ldr + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(v + p.add);
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
+                                        const Pre& p) const {
+    out[(int64_t)m * ldo + n] = from_f32<OutT>(v + c.b + p.r);
   }
 };
 
@@ -152,10 +161,13 @@ template <typename T>
 struct EpiAct {
   T* u; T* a_keep; int64_t ldo; const T* bias; int act;
   static constexpr bool kPair = false;
-  struct Pre { float b; };
-  __device__ __forceinline__ Pre pre(int, int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
-    v += p.b;
+  struct Col { float b; };
+  struct Pre {};
+  __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
+  __device__ __forceinline__ Pre pre(int, int, const Col&) const { return {}; }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
+                                        const Pre&) const {
+    v += c.b;
     const int64_t i = (int64_t)m * ldo + n;
     if (a_keep) a_keep[i] = from_f32<T>(v);
     u[i] = from_f32<T>(act == ACT_RELU ? act_relu(v) : act_gelu(v));
@@ -167,11 +179,14 @@ template <typename T>
 struct EpiSwiUp {
   T* u; T* up_keep; const T* gate; int64_t ldo;
   static constexpr bool kPair = false;
+  struct Col {};
   struct Pre { float g; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
+  __device__ __forceinline__ Col col(int) const { return {}; }
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {to_f32(gate[(int64_t)m * ldo + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
+                                        const Pre& p) const {
     const int64_t i = (int64_t)m * ldo + n;
     if (up_keep) up_keep[i] = from_f32<T>(v);
     u[i] = from_f32<T>(p.g * sigmoidf_(p.g) * v);
@@ -183,11 +198,14 @@ template <typename T>
 struct EpiActGrad {
   T* da; const T* a; int64_t ldo; int act;
   static constexpr bool kPair = false;
+  struct Col {};
   struct Pre { float x; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
+  __device__ __forceinline__ Col col(int) const { return {}; }
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {to_f32(a[(int64_t)m * ldo + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
+                                        const Pre& p) const {
     const float gr = act == ACT_RELU ? (p.x > 0.f ? 1.f : 0.f) : act_gelu_grad(p.x);
     da[(int64_t)m * ldo + n] = from_f32<T>(v * gr);
   }
@@ -199,12 +217,15 @@ template <typename T>
 struct EpiSwiGrad {
   T* dgate; T* dup; const T* gate; const T* up; int64_t ldo;
   static constexpr bool kPair = false;
+  struct Col {};
   struct Pre { float g, u; };
-  __device__ __forceinline__ Pre pre(int m, int n) const {
+  __device__ __forceinline__ Col col(int) const { return {}; }
+  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     const int64_t i = (int64_t)m * ldo + n;
     return {to_f32(gate[i]), to_f32(up[i])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Pre& p) const {
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
+                                        const Pre& p) const {
     const int64_t i = (int64_t)m * ldo + n;
     const float sg = sigmoidf_(p.g);
     dgate[i] = from_f32<T>(v * p.u * sg * (1.f + p.g * (1.f - sg)));
@@ -213,15 +234,18 @@ struct EpiSwiGrad {
 };
 
 // Epilogue of one 32 x 32 accumulator block (rows m0 + acc_row(r, g), column
-// col of this lane): gather, then apply.
+// col of this lane). Inputs are gathered from indices clamped into the
+// matrix (M, N > 0), so the loads need no branches; only stores are guarded.
 template <bool EVEN, class Epi>
 __device__ __forceinline__ void epilogue_block(const Epi& epi, const f32x16& acc, int m0, int col,
                                                int g, int M, int N) {
+  const int cq = EVEN ? col : min(col, N - 1);
+  const typename Epi::Col cv = epi.col(cq);
   typename Epi::Pre pre[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + acc_row(r, g);
-    if (EVEN || (row < M && col < N)) pre[r] = epi.pre(row, col);
+    pre[r] = epi.pre(EVEN ? row : min(row, M - 1), cq, cv);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -229,7 +253,7 @@ __device__ __forceinline__ void epilogue_block(const Epi& epi, const f32x16& acc
     const float v = acc[r];
     float vp = 0.f;
     if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
-    if (EVEN || (row < M && col < N)) epi.apply(row, col, v, vp, pre[r]);
+    if (EVEN || (row < M && col < N)) epi.apply(row, col, v, vp, cv, pre[r]);
   }
 }
 
