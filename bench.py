@@ -97,8 +97,8 @@ def cpu_baseline(sh, sample_len: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt1b-s128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
@@ -199,6 +199,10 @@ def main() -> int:
     print(f"[bench] step {ms_per_step:.2f} ms (wall {wall_ms:.2f}); fwd {np.mean(fwd_ms):.2f} "
           f"bwd {np.mean(bwd_ms):.2f}; timing {timing}", file=sys.stderr, flush=True)
 
+    # Sustained MFMA rate of this device (a register-only MFMA kernel), the
+    # practical ceiling next to the datasheet peak.
+    practical = bpt.bpt_mfma_peak_probe(stream) if sh.dtype == "bf16" else None
+
     fl = model_flops(sh)
     tokens = sh.seq_len * sh.batch
     tflops = fl["step"] / (ms_per_step * 1e-3) / 1e12
@@ -240,8 +244,12 @@ def main() -> int:
                    "head_dim": sh.head_dim, "ffn_dim": sh.ffn_dim, "ffn": sh.ffn, "norm": sh.norm,
                    "causal": sh.causal, "rope_base": sh.rope_base, "q_block": sh.q_block,
                    "kv_block": sh.kv_block, "head_chunk": sh.head_chunk},
+        "ms_per_step_median": round(float(np.median(step_ms)), 3),
+        "ms_per_step_min": round(float(np.min(step_ms)), 3),
         "model_tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak, 4),
+        "mfma_practical_peak_tflops": round(practical, 1) if practical else None,
+        "mfma_practical_frac": round(tflops / practical, 4) if practical else None,
         "fwd_ms": round(float(np.mean(fwd_ms)), 3),
         "bwd_ms": round(float(np.mean(bwd_ms)), 3),
         "kernel_ms_per_step": breakdown,

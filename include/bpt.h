@@ -162,6 +162,14 @@ bpt_status bpt_timing_enable(uint32_t class_mask);
  * event query fails. */
 bpt_status bpt_timing_read(double* total_ms, int64_t* launches, int32_t reset);
 
+/* ---- Measurement helper ----
+ * Dense bf16 MFMA throughput the current device sustains, in TFLOP/s: runs
+ * (synchronously, on `stream`) a kernel of independent 32x32x16 bf16 MFMA
+ * chains on every CU, two waves per SIMD, and times it with HIP events. Used
+ * to report utilisation against a practical peak next to the datasheet one.
+ * Allocates no device memory; BPT_EHIP if the launch or timing fails. */
+bpt_status bpt_mfma_peak_probe(double* tflops, void* stream);
+
 /* Message of the last failing call on this host thread ("" if none). */
 const char* bpt_last_error(void);
 

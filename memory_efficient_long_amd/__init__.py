@@ -19,6 +19,7 @@ __all__ = [
     "load_library", "bpt_layer_validate", "bpt_layer_saved_size", "bpt_layer_workspace_size",
     "bpt_layer_forward", "bpt_layer_backward", "bpt_status_string", "bpt_last_error",
     "forward", "backward", "WEIGHT_NAMES", "GRAD_NAMES", "bpt_timing_enable", "bpt_timing_read",
+    "bpt_mfma_peak_probe",
     "KERNEL_CLASSES",
 ]
 
@@ -99,6 +100,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bpt_status_string.restype = ctypes.c_char_p
     lib.bpt_last_error.argtypes = []
     lib.bpt_last_error.restype = ctypes.c_char_p
+    lib.bpt_mfma_peak_probe.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.bpt_mfma_peak_probe.restype = ctypes.c_int
     lib.bpt_timing_enable.argtypes = [ctypes.c_uint32]
     lib.bpt_timing_enable.restype = ctypes.c_int
     lib.bpt_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int32]
@@ -195,6 +198,15 @@ def bpt_timing_read(reset: bool = True) -> Dict[str, tuple]:
     if st:
         raise BptError(st, "bpt_timing_read")
     return {c: (ms[i], cnt[i]) for i, c in enumerate(KERNEL_CLASSES)}
+
+
+def bpt_mfma_peak_probe(stream=None) -> float:
+    """Sustained dense bf16 MFMA TFLOP/s of the current device (measured)."""
+    out = ctypes.c_double(0.0)
+    st = load_library().bpt_mfma_peak_probe(ctypes.byref(out), _stream_handle(stream))
+    if st:
+        raise BptError(st, "bpt_mfma_peak_probe")
+    return out.value
 
 
 def _weights_struct(weights: Dict[str, "object"]) -> BptLayerWeights:

@@ -29,6 +29,7 @@
 #include "attention.hpp"
 #include "attention_dma.hpp"
 #include "gemm_dma.hpp"
+#include "peak.hpp"
 #include "gemm.hpp"
 #include "rowwise.hpp"
 
@@ -820,6 +821,31 @@ bpt_status bpt_timing_enable(uint32_t class_mask) {
   std::lock_guard<std::mutex> lk(t.mu);
   t.mask = class_mask & ((1u << BPT_KERNEL_CLASSES) - 1);
   return BPT_OK;
+}
+
+bpt_status bpt_mfma_peak_probe(double* tflops, void* stream) {
+  if (!tflops) return fail(BPT_EINVAL, "tflops is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  const int cus = device_cus();
+  const int iters = 2048;
+  const dim3 grid((unsigned)(2 * cus)), blk(256);  // two waves per SIMD
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return fail(BPT_EHIP, "hipEventCreate");
+  if (hipEventCreate(&e1) != hipSuccess) { hipEventDestroy(e0); return fail(BPT_EHIP, "hipEventCreate"); }
+  hipLaunchKernelGGL(mfma_peak_kernel, grid, blk, 0, st, iters, 1e-3f);  // warm-up
+  hipEventRecord(e0, st);
+  hipLaunchKernelGGL(mfma_peak_kernel, grid, blk, 0, st, iters, 1e-3f);
+  hipEventRecord(e1, st);
+  bpt_status res = BPT_OK;
+  float ms = 0.f;
+  if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess ||
+      hipGetLastError() != hipSuccess || ms <= 0.f)
+    res = fail(BPT_EHIP, "mfma peak probe failed");
+  else
+    *tflops = (double)grid.x * 4.0 * iters * 8.0 * (2.0 * 32 * 32 * 16) / (ms * 1e-3) / 1e12;
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return res;
 }
 
 bpt_status bpt_timing_read(double* total_ms, int64_t* launches, int32_t reset) {
