@@ -548,17 +548,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
       const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        f32x16 sacc = zero16(), dpacc = zero16();
+        // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc.
+        f32x16 sacc = zero16(), dpacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpacc[r] = -dd_q;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
           dpacc = mma(TL::frag_at(vsa + buf * TB, rf, sb, c), df[c], dpacc);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
-          dpacc[r] = p * (dpacc[r] - dd_q);
-        }
+        for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(fmaf(sacc[r], sl2, -lse_q));
         if (MASK) {
           const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb - 32 * sb;
 #pragma unroll
