@@ -296,15 +296,18 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
   TimedLaunch tl(BPT_KERNEL_GEMM, st);
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0) {
-      // Direct-to-LDS pipelines. Shapes with at least one 256 x 256 tile per
-      // CU use 8 waves of 64 x 128 (half the L2 -> LDS traffic per flop of a
-      // 128 x 128 tile); smaller outputs use 128 x 128 tiles of 4 waves, two
-      // workgroups per CU.
+      // Direct-to-LDS pipelines, 8 waves per workgroup. Shapes with at least
+      // one 256 x 256 tile per CU use waves of 64 x 128 (half the L2 -> LDS
+      // traffic per flop of a 128 x 128 tile); smaller outputs use 128 x 128
+      // tiles (waves of 32 x 64) to keep every CU busy.
       const int64_t nt256 = ((M + 255) / 256) * ((N + 255) / 256);
       if (nt256 >= device_cus()) {
         launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, epi);
+      } else if (K >= 32768) {
+        // long reductions (weight gradients over the sequence): three stages
+        launch_gemm_dma<AK, BK, 128, 128, 64, 3, 64, 32, 8>(st, A, lda, B, ldb, M, N, K, epi);
       } else {
-        launch_gemm_dma<AK, BK, 128, 128, 64, 2, 64, 64, 4>(st, A, lda, B, ldb, M, N, K, epi);
+        launch_gemm_dma<AK, BK, 128, 128, 64, 2, 32, 64, 8>(st, A, lda, B, ldb, M, N, K, epi);
       }
       return check_launch(what);
     }
