@@ -410,6 +410,34 @@ bpt_status rope_table(hipStream_t st, const Plan& p, float2* tab) {
   return check_launch("rope_table");
 }
 
+#ifndef BPT_ATTN_WAVES
+#define BPT_ATTN_WAVES 4
+#endif
+#ifndef BPT_ATTN_STAGES
+#define BPT_ATTN_STAGES 2
+#endif
+// Forward attention: waves per workgroup and K/V ring depth. Four waves with
+// two slots (two workgroups per CU) measured fastest; eight waves with three
+// slots halve the L2 -> LDS bytes but leave one workgroup per CU, whose
+// barrier waits then idle the SIMDs.
+constexpr int kAttnWaves = BPT_ATTN_WAVES, kAttnStages = BPT_ATTN_STAGES;
+
+// Launch a direct-load attention kernel over heads x ceil(s / rows) tiles with
+// its K/V (or Q/dO) ring in dynamic shared memory (2 slots' worth of tiles per
+// stage: one K and one V, or one Q and one dO, tile of 64 rows x D).
+template <auto Kern, int D, class Args>
+bpt_status launch_attn_dma(hipStream_t st, int64_t heads, int64_t s, int rows, const Args& a,
+                           const char* what) {
+  constexpr int kLds = kAttnStages * 2 * 64 * D * 2;
+  static std::once_flag attr_once;  // per instantiation
+  std::call_once(attr_once, [&] {
+    (void)hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  });
+  const dim3 grid((unsigned)(heads * ((s + rows - 1) / rows))), blk(64 * kAttnWaves);
+  hipLaunchKernelGGL(Kern, grid, blk, kLds, st, a);
+  return check_launch(what);
+}
+
 template <typename T>
 bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v, T* o,
                     float* lse) {
@@ -420,8 +448,10 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
   if constexpr (sizeof(T) == 2) {
-    if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
-    if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
+    if (p.D == 128) return launch_attn_dma<attn_fwd_dma_kernel<128, kAttnWaves, kAttnStages>, 128>(
+        st, p.U, p.s, 32 * kAttnWaves, a, "attn_fwd");
+    if (p.D == 64) return launch_attn_dma<attn_fwd_dma_kernel<64, kAttnWaves, kAttnStages>, 64>(
+        st, p.U, p.s, 32 * kAttnWaves, a, "attn_fwd");
   }
   if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<T, 32>), grid, blk, 0, st, a);
