@@ -106,6 +106,24 @@ SMALL: Dict[str, LayerShape] = {
     "llama70b-small": WORKLOADS["llama70b-s8k"].replace(
         name="llama70b-small", seq_len=400, hidden=1024, n_heads=8, n_kv_heads=2,
         ffn_dim=2816, q_block=200, kv_block=400, head_chunk=8),
+    # Code paths the five workloads do not reach: head_dim 64 and 32 in bf16,
+    # attention without the causal mask, fp32 with GQA and RoPE. (ReLU is run
+    # in fp32 only: in bf16 the pre-activation is recomputed from bf16-stored
+    # values, and where it lies within rounding of 0 the ReLU derivative flips,
+    # an O(1) difference per such element that no tolerance on rounding covers.)
+    "bf16-d64-noncausal": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d64-noncausal", seq_len=336, hidden=256, n_heads=4, n_kv_heads=4,
+        head_dim=64, ffn_dim=512, causal=False, q_block=112, kv_block=168, head_chunk=4),
+    "bf16-d64-gqa-rope": WORKLOADS["llama8b-s64k"].replace(
+        name="bf16-d64-gqa-rope", seq_len=400, hidden=256, n_heads=4, n_kv_heads=2,
+        head_dim=64, ffn_dim=768, q_block=200, kv_block=400, head_chunk=2),
+    "bf16-d32": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d32", seq_len=272, hidden=128, n_heads=4, n_kv_heads=4, head_dim=32,
+        ffn_dim=512, q_block=136, kv_block=272, head_chunk=2),
+    "f32-d64-gqa-rope-noncausal": WORKLOADS["gpt-tiny-fp32"].replace(
+        name="f32-d64-gqa-rope-noncausal", seq_len=240, hidden=256, n_heads=4, n_kv_heads=2,
+        head_dim=64, ffn_dim=512, norm="rmsnorm", ffn="gelu", causal=False,
+        rope_base=10000.0, q_block=120, kv_block=80, head_chunk=2),
 }
 
 
