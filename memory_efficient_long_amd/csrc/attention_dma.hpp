@@ -175,26 +175,16 @@ struct DmaTile {
 
 
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
-// Wait until at most N vector-memory operations (direct loads) of this wave
-// are in flight and all of its LDS operations are done. Loads complete in
-// issue order, so this leaves the N most recently issued ones outstanding.
-template <int N>
-__device__ __forceinline__ void wait_dma_keep() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
 
 // ============================================================================ forward
-// NW waves (32 query rows each) share one K/V stream through an ST-slot LDS
-// ring (dynamic shared memory, 2 ST tile bytes): tile t + ST - 1 is loaded
-// while tile t is consumed.
-template <int D, int NW, int ST>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> a) {
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> a) {
   using TL = DmaTile<D>;
-  constexpr int BQ = 32 * NW, BKV = 64;
+  constexpr int BQ = 128, BKV = 64;
   constexpr int NC = D / 16, ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 ks[2][BKV * D];
+  __shared__ __attribute__((aligned(1024))) bf16 vs[2][BKV * D];
   constexpr uint32_t TB = BKV * D * 2;  // tile bytes
-  extern __shared__ __attribute__((aligned(1024))) char attn_smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, g = lane >> 5;
@@ -226,30 +216,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_dma_kernel(AttnFwdAr
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  const uint32_t ksa = lds_addr(attn_smem), vsa = ksa + ST * TB;
+  const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
   const uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
-  using Ld = typename TL::template Loader<BKV, NW>;
-  constexpr int LPT = 2 * Ld::PERW;  // direct loads per wave per K+V tile
-  const Ld kvld(D, lane);
-#pragma unroll
-  for (int j = 0; j < ST - 1; ++j)
-    if (j < ntiles) {
-      kvld.issue(ksa + j * TB, Kp, j * BKV, s, w, lane);
-      kvld.issue(vsa + j * TB, Vp, j * BKV, s, w, lane);
-    }
-  if (ntiles >= ST - 1) wait_dma_keep<(ST - 2) * LPT>();
-  else wait_dma();
+  const typename TL::template Loader<BKV, 4> kvld(D, lane);
+  if (ntiles > 0) {
+    kvld.issue(ksa, Kp, 0, s, w, lane);
+    kvld.issue(vsa, Vp, 0, s, w, lane);
+  }
+  wait_dma();
   __syncthreads();
 
-  // One key tile per call; the ring slot is a compile-time constant (the
-  // loop below is unrolled by ST), so every LDS address is a per-lane base
+  // One key tile per call; the buffer index is a compile-time constant (the
+  // loop below is unrolled by two), so every LDS address is a per-lane base
   // held in a register plus an immediate offset.
   auto tile_step = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    constexpr int nbuf = (buf + ST - 1) % ST;
-    if (t + ST - 1 < ntiles) {
-      kvld.issue(ksa + nbuf * TB, Kp, (t + ST - 1) * BKV, s, w, lane);
-      kvld.issue(vsa + nbuf * TB, Vp, (t + ST - 1) * BKV, s, w, lane);
+    if (t + 1 < ntiles) {
+      kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
+      kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
     }
     if (wave_active && t < wave_tiles) {
       const int kvb = t * BKV;
@@ -308,17 +292,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_dma_kernel(AttnFwdAr
         for (int i = 0; i < ND; ++i)
           oacc[i] = mma(TL::template tr_at<false>(vsa + buf * TB, trb, cc, i), pf[cc], oacc[i]);
     }
-    // Tile t + 1 must be resident for the next step; the loads of later tiles
-    // may stay in flight.
-    if (t + ST - 1 < ntiles) wait_dma_keep<(ST - 2) * LPT>();
-    else wait_dma();
+    wait_dma();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += ST) {
+  for (int t = 0; t < ntiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>());
     if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
-    if constexpr (ST > 2)
-      if (t + 2 < ntiles) tile_step(t + 2, std::integral_constant<int, 2>());
   }
 
   if (wave_active && qrow < s) {

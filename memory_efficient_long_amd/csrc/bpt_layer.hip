@@ -96,6 +96,11 @@ struct TimedLaunch {
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
 constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
+// The backward keeps the FFN activations of up to this many consecutive query
+// blocks so that each fp32 weight-gradient GEMM reduces over the whole group:
+// one read-modify-write of dW_1 / dW_2 per group instead of one per block. The
+// per-block FFN arithmetic is unchanged.
+constexpr int64_t kGradGroupBlocks = 4;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -103,6 +108,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Plan {
   int dtype, norm, ffn, causal, rope;
   int64_t b, s, h, H, Hkv, D, f, cq, ckv, U, G, nkvc, qkv_cols, chunk_cols;
+  int64_t gq;  // query blocks per weight-gradient group (backward)
   double rope_base;
   float eps;
   size_t esz;  // storage element size
@@ -149,6 +155,7 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
   p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
   p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
   p.chunk_cols = (p.U + 2 * p.nkvc) * p.D;
+  p.gq = std::min<int64_t>(p.s / p.cq, kGradGroupBlocks);
   p.rope_base = d->rope_base; p.eps = d->norm_eps;
   p.esz = d->dtype == BPT_BF16 ? 2 : 4;
   return BPT_OK;
@@ -209,12 +216,15 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.v = c.take<T>(p.nkvc * p.s * p.D);
   w.dqkv = c.take<T>(p.s * p.chunk_cols);
   w.h1 = c.take<float>(p.s * p.h);  // recomputed x + O W_o + b_o, whole sequence
-  w.z = c.take<T>(p.cq * p.h);
+  // z, u, da (and the SwiGLU up-gradient) for a group of gq query blocks;
+  // the pre-activations are per block.
+  const int64_t grp = p.gq * p.cq;
+  w.z = c.take<T>(grp * p.h);
   w.a = c.take<T>(p.cq * p.f);
-  w.u = c.take<T>(p.cq * p.f);
+  w.u = c.take<T>(grp * p.f);
   w.up = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
-  w.da = c.take<T>(p.cq * p.f);
-  w.dup = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  w.da = c.take<T>(grp * p.f);
+  w.dup = p.ffn == BPT_SWIGLU ? c.take<T>(grp * p.f) : nullptr;
   w.dz = c.take<float>(p.cq * p.h);
   w.dh_t = c.take<T>(p.s * p.h);  // dh in the storage type, whole sequence
   const int64_t maxn = std::max<int64_t>(std::max(p.h, p.f), std::max(p.chunk_cols, HD));
@@ -410,34 +420,6 @@ bpt_status rope_table(hipStream_t st, const Plan& p, float2* tab) {
   return check_launch("rope_table");
 }
 
-#ifndef BPT_ATTN_WAVES
-#define BPT_ATTN_WAVES 4
-#endif
-#ifndef BPT_ATTN_STAGES
-#define BPT_ATTN_STAGES 2
-#endif
-// Forward attention: waves per workgroup and K/V ring depth. Four waves with
-// two slots (two workgroups per CU) measured fastest; eight waves with three
-// slots halve the L2 -> LDS bytes but leave one workgroup per CU, whose
-// barrier waits then idle the SIMDs.
-constexpr int kAttnWaves = BPT_ATTN_WAVES, kAttnStages = BPT_ATTN_STAGES;
-
-// Launch a direct-load attention kernel over heads x ceil(s / rows) tiles with
-// its K/V (or Q/dO) ring in dynamic shared memory (2 slots' worth of tiles per
-// stage: one K and one V, or one Q and one dO, tile of 64 rows x D).
-template <auto Kern, int D, class Args>
-bpt_status launch_attn_dma(hipStream_t st, int64_t heads, int64_t s, int rows, const Args& a,
-                           const char* what) {
-  constexpr int kLds = kAttnStages * 2 * 64 * D * 2;
-  static std::once_flag attr_once;  // per instantiation
-  std::call_once(attr_once, [&] {
-    (void)hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  });
-  const dim3 grid((unsigned)(heads * ((s + rows - 1) / rows))), blk(64 * kAttnWaves);
-  hipLaunchKernelGGL(Kern, grid, blk, kLds, st, a);
-  return check_launch(what);
-}
-
 template <typename T>
 bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v, T* o,
                     float* lse) {
@@ -448,10 +430,8 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
   if constexpr (sizeof(T) == 2) {
-    if (p.D == 128) return launch_attn_dma<attn_fwd_dma_kernel<128, kAttnWaves, kAttnStages>, 128>(
-        st, p.U, p.s, 32 * kAttnWaves, a, "attn_fwd");
-    if (p.D == 64) return launch_attn_dma<attn_fwd_dma_kernel<64, kAttnWaves, kAttnStages>, 64>(
-        st, p.U, p.s, 32 * kAttnWaves, a, "attn_fwd");
+    if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
+    if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
   }
   if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
   else hipLaunchKernelGGL((attn_fwd_kernel<T, 32>), grid, blk, 0, st, a);
@@ -630,57 +610,70 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
       BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection (re)")));
     }
-    // ---- per query block: FFN and Norm2 backward
+    // ---- per query block: FFN and Norm2 backward. The FFN activations of a
+    // group of gq consecutive blocks stay in the workspace; the weight
+    // gradients are accumulated once per group.
     int np_db1 = 0, np_n2 = 0;
+    const int64_t grp = p.gq * p.cq;
     for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
       const T* dyi = dyb + r0 * p.h;
       const float* h1i = w.h1 + r0 * p.h;
-      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, w.z, p.h, p.cq)));
+      const int64_t o = r0 % grp;  // row of this block within the group buffers
+      T* zi = w.z + o * p.h;
+      T* ui = w.u + o * p.f;
+      T* dai = w.da + o * p.f;
+      T* dupi = w.dup ? w.dup + o * p.f : nullptr;
+      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, zi, p.h, p.cq)));
       if (swiglu) {
         EpiOut<T, T> eg{w.a, p.f, b1, 1.f, 0};   // w.a holds the gate pre-activation
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate (re)")));
-        EpiSwiUp<T> eu{w.u, w.up, w.a, p.f};
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up (re)")));
+        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate (re)")));
+        EpiSwiUp<T> eu{ui, w.up, w.a, p.f};
+        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up (re)")));
       } else {
-        EpiAct<T> ea{w.u, w.a, p.f, b1, act};
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1 (re)")));
-      }
-      if (dw2) {
-        EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyi, p.h, p.f, p.h, p.cq, e, "dW2")));
+        EpiAct<T> ea{ui, w.a, p.f, b1, act};
+        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1 (re)")));
       }
       if (swiglu) {
-        EpiSwiGrad<T> e{w.da, w.dup, w.a, w.up, p.f};
+        EpiSwiGrad<T> e{dai, dupi, w.a, w.up, p.f};
         BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du (swiglu)")));
       } else {
-        EpiActGrad<T> e{w.da, w.a, p.f, act};
+        EpiActGrad<T> e{dai, w.a, p.f, act};
         BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du")));
-      }
-      if (dw1) {
-        EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, p.cq, e, "dW1")));
-      }
-      if (dw3) {
-        EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, p.cq, e, "dW3")));
       }
       // Bias and norm-parameter gradients of the block: partial column sums
       // accumulate over the blocks and are reduced after the last one.
       const int first = r0 == 0 ? 0 : 1;
       const bool last = r0 + p.cq >= p.s;
-      BPT_TRY(colsum<T>(st, w.da, p.f, p.cq, p.f, w.part, db1, first, last, &np_db1));
+      BPT_TRY(colsum<T>(st, dai, p.f, p.cq, p.f, w.part, db1, first, last, &np_db1));
       {
         EpiOut<T, float> e{w.dz, p.h, nullptr, 1.f, 0};
-        BPT_TRY((gemm<T, true, true>(st, w.da, p.f, w1, p.f, p.cq, p.h, p.f, e, "dz")));
+        BPT_TRY((gemm<T, true, true>(st, dai, p.f, w1, p.f, p.cq, p.h, p.f, e, "dz")));
         if (swiglu) {
           EpiOut<T, float> e3{w.dz, p.h, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, true, true>(st, w.dup, p.f, w3, p.f, p.cq, p.h, p.f, e3, "dz (up)")));
+          BPT_TRY((gemm<T, true, true>(st, dupi, p.f, w3, p.f, p.cq, p.h, p.f, e3, "dz (up)")));
         }
       }
       float* dh_rows = w.dh + r0 * p.h;
       BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, h1i, p.h, g2, dyi, p.h, dh_rows,
                                      w.dh_t + r0 * p.h, p.h, p.cq, dg2, dsh2, w.npart_g,
                                      w.npart_b, first, last, &np_n2)));
+      // Weight gradients of the group, reduced over all of its rows.
+      if (o + p.cq == grp || last) {
+        const int64_t rows = o + p.cq, g0 = r0 + p.cq - rows;
+        if (dw2) {
+          EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyb + g0 * p.h, p.h, p.f, p.h, rows, e,
+                                         "dW2")));
+        }
+        if (dw1) {
+          EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, rows, e, "dW1")));
+        }
+        if (dw3) {
+          EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
+          BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, rows, e, "dW3")));
+        }
+      }
     }
     // ---- O-projection backward over the whole sequence: dW_o += O^T dh,
     // dO = dh W_o^T.
