@@ -143,14 +143,26 @@ struct DmaTile {
       l0 = (uint32_t)(j * ldb) + 16u * ((lane % CPR) ^ f(j));
     }
     // Rows [row0, row0 + R) of src into the tile at LDS address `tile`; rows
-    // at or past rlim repeat row rlim - 1 (masked by the caller).
+    // at or past rlim repeat row rlim - 1 (masked by the caller). LAZY: the
+    // lane offset is recomputed from the lane id here instead of being read
+    // from l0, for kernels where keeping it live across the loop would spill
+    // it (a spill reload after these loads would wait for them).
+    template <bool LAZY = false>
     __device__ __forceinline__ void issue(uint32_t tile, const bf16* src, int row0, int rlim, int w,
                                           int lane) const {
       // The empty asm statements make the lane values opaque at each call, so
       // the per-load offsets are recomputed here (one VALU op each) rather
       // than hoisted out of the caller's loop into registers of their own.
       if (row0 + R <= rlim) {
-        uint32_t l = l0;
+        uint32_t l;
+        if constexpr (LAZY) {
+          int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+          asm volatile("" : "+v"(ln));
+          const int j = ln / CPR;
+          l = (uint32_t)(j * ldb) + 16u * ((ln % CPR) ^ f(j));
+        } else {
+          l = l0;
+        }
         asm volatile("" : "+v"(l));
         const char* base = (const char*)src + (int64_t)row0 * ldb;
 #pragma unroll
@@ -159,7 +171,8 @@ struct DmaTile {
           dma16_s(base + brow * ldb, l ^ (16u * f(brow)), tile + (w * PERW + m) * 1024);
         }
       } else {
-        int ln = lane;
+        int ln = LAZY ? (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))
+                      : lane;
         asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int m = 0; m < PERW; ++m) {
@@ -344,6 +357,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     kf[c] = kvrow < s ? ld_frag(Kp + (int64_t)kvrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
     vf[c] = kvrow < s ? ld_frag(Vp + (int64_t)kvrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
   }
+  // The last KPARK K fragments are parked in LDS and read back where they are
+  // used: the registers they free keep the loop free of spills, whose reloads
+  // (counted with the direct loads by vmcnt) would wait for the tile loads.
+  // Two measured best (8 KiB per workgroup; four would leave room for only one
+  // workgroup per CU).
+  constexpr int KPARK = 2;
+  __shared__ __attribute__((aligned(16))) bf16x8 kpark[KPARK > 0 ? KPARK : 1][4][64];
+#pragma unroll
+  for (int c = 0; c < KPARK; ++c) kpark[c][w][lane] = kf[NC - KPARK + c];
+  const uint32_t kpa = lds_addr(&kpark[0][w][lane]);
 
   f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
@@ -371,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       lse_r = valid_r ? a.lse[(int64_t)hq * s + qr] : 0.f;
       dd_r = valid_r ? a.dvec[(int64_t)hq * s + qr] : 0.f;
     }
-    qld.issue(qsa + buf * TB, a.q + (int64_t)hq * s * D, q0, s, w, lane);
-    dold.issue(dosa + buf * TB, a.dout + (int64_t)hq * D, q0, s, w, lane);
+    qld.template issue<true>(qsa + buf * TB, a.q + (int64_t)hq * s * D, q0, s, w, lane);
+    dold.template issue<true>(dosa + buf * TB, a.dout + (int64_t)hq * D, q0, s, w, lane);
   };
   // Stored negated (the LSE in units of the raw score) to seed the S and dP
   // accumulators; rows past the end get -inf (P = 0) and 0.
@@ -413,7 +436,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc = mma(TL::frag_at(qsa + buf * TB, rf, qb, c), kf[c], sacc);
+        bf16x8 kc = kf[c];
+        if (c >= NC - KPARK) {
+          uint32_t pa = kpa + (c - (NC - KPARK)) * (4 * 64 * 16);
+          asm volatile("" : "+v"(pa));
+          kc = *(const __attribute__((address_space(3))) bf16x8*)(size_t)pa;
+        }
+        sacc = mma(TL::frag_at(qsa + buf * TB, rf, qb, c), kc, sacc);
         dpacc = mma(TL::frag_at(dosa + buf * TB, rf, qb, c), vf[c], dpacc);
       }
 #pragma unroll
