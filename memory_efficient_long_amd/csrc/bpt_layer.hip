@@ -96,10 +96,10 @@ struct TimedLaunch {
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
 constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
-// The backward keeps the FFN activations of up to this many consecutive query
-// blocks so that each fp32 weight-gradient GEMM reduces over the whole group:
-// one read-modify-write of dW_1 / dW_2 per group instead of one per block. The
-// per-block FFN arithmetic is unchanged.
+// The backward runs the FFN recompute and backward on groups of up to this
+// many consecutive query blocks: GEMMs four times taller, a quarter of the
+// launches, and one read-modify-write of the fp32 dW_1 / dW_2 per group. The
+// FFN scratch stays O(c_q f) (no s x f term); the forward keeps one block.
 constexpr int64_t kGradGroupBlocks = 4;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -216,16 +216,15 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.v = c.take<T>(p.nkvc * p.s * p.D);
   w.dqkv = c.take<T>(p.s * p.chunk_cols);
   w.h1 = c.take<float>(p.s * p.h);  // recomputed x + O W_o + b_o, whole sequence
-  // z, u, da (and the SwiGLU up-gradient) for a group of gq query blocks;
-  // the pre-activations are per block.
+  // FFN activations and gradients for a group of gq query blocks.
   const int64_t grp = p.gq * p.cq;
   w.z = c.take<T>(grp * p.h);
-  w.a = c.take<T>(p.cq * p.f);
+  w.a = c.take<T>(grp * p.f);
   w.u = c.take<T>(grp * p.f);
-  w.up = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  w.up = p.ffn == BPT_SWIGLU ? c.take<T>(grp * p.f) : nullptr;
   w.da = c.take<T>(grp * p.f);
   w.dup = p.ffn == BPT_SWIGLU ? c.take<T>(grp * p.f) : nullptr;
-  w.dz = c.take<float>(p.cq * p.h);
+  w.dz = c.take<float>(grp * p.h);
   w.dh_t = c.take<T>(p.s * p.h);  // dh in the storage type, whole sequence
   const int64_t maxn = std::max<int64_t>(std::max(p.h, p.f), std::max(p.chunk_cols, HD));
   w.part = c.take<float>(kColsumParts * maxn);
@@ -610,69 +609,56 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
       BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection (re)")));
     }
-    // ---- per query block: FFN and Norm2 backward. The FFN activations of a
-    // group of gq consecutive blocks stay in the workspace; the weight
-    // gradients are accumulated once per group.
+    // ---- FFN and Norm2 backward, a group of gq consecutive query blocks at
+    // a time (the whole FFN chain of the group, then its weight gradients).
     int np_db1 = 0, np_n2 = 0;
     const int64_t grp = p.gq * p.cq;
-    for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
-      const T* dyi = dyb + r0 * p.h;
-      const float* h1i = w.h1 + r0 * p.h;
-      const int64_t o = r0 % grp;  // row of this block within the group buffers
-      T* zi = w.z + o * p.h;
-      T* ui = w.u + o * p.f;
-      T* dai = w.da + o * p.f;
-      T* dupi = w.dup ? w.dup + o * p.f : nullptr;
-      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, zi, p.h, p.cq)));
+    for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
+      const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
+      const T* dyg = dyb + g0 * p.h;
+      const float* h1g = w.h1 + g0 * p.h;
+      BPT_TRY((norm_fwd<T, float, T>(st, p, h1g, p.h, g2, sh2, w.z, p.h, rows)));
       if (swiglu) {
         EpiOut<T, T> eg{w.a, p.f, b1, 1.f, 0};   // w.a holds the gate pre-activation
-        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate (re)")));
-        EpiSwiUp<T> eu{ui, w.up, w.a, p.f};
-        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up (re)")));
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, rows, p.f, p.h, eg, "ffn gate (re)")));
+        EpiSwiUp<T> eu{w.u, w.up, w.a, p.f};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, rows, p.f, p.h, eu, "ffn up (re)")));
+        EpiSwiGrad<T> e{w.da, w.dup, w.a, w.up, p.f};
+        BPT_TRY((gemm<T, true, true>(st, dyg, p.h, w2, p.h, rows, p.f, p.h, e, "du (swiglu)")));
       } else {
-        EpiAct<T> ea{ui, w.a, p.f, b1, act};
-        BPT_TRY((gemm<T, true, false>(st, zi, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1 (re)")));
+        EpiAct<T> ea{w.u, w.a, p.f, b1, act};
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, rows, p.f, p.h, ea, "ffn fc1 (re)")));
+        EpiActGrad<T> e{w.da, w.a, p.f, act};
+        BPT_TRY((gemm<T, true, true>(st, dyg, p.h, w2, p.h, rows, p.f, p.h, e, "du")));
       }
-      if (swiglu) {
-        EpiSwiGrad<T> e{dai, dupi, w.a, w.up, p.f};
-        BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du (swiglu)")));
-      } else {
-        EpiActGrad<T> e{dai, w.a, p.f, act};
-        BPT_TRY((gemm<T, true, true>(st, dyi, p.h, w2, p.h, p.cq, p.f, p.h, e, "du")));
-      }
-      // Bias and norm-parameter gradients of the block: partial column sums
-      // accumulate over the blocks and are reduced after the last one.
-      const int first = r0 == 0 ? 0 : 1;
-      const bool last = r0 + p.cq >= p.s;
-      BPT_TRY(colsum<T>(st, dai, p.f, p.cq, p.f, w.part, db1, first, last, &np_db1));
+      // Bias and norm-parameter gradients: partial column sums accumulate over
+      // the groups and are reduced after the last one.
+      const int first = g0 == 0 ? 0 : 1;
+      const bool last = g0 + rows >= p.s;
+      BPT_TRY(colsum<T>(st, w.da, p.f, rows, p.f, w.part, db1, first, last, &np_db1));
       {
         EpiOut<T, float> e{w.dz, p.h, nullptr, 1.f, 0};
-        BPT_TRY((gemm<T, true, true>(st, dai, p.f, w1, p.f, p.cq, p.h, p.f, e, "dz")));
+        BPT_TRY((gemm<T, true, true>(st, w.da, p.f, w1, p.f, rows, p.h, p.f, e, "dz")));
         if (swiglu) {
           EpiOut<T, float> e3{w.dz, p.h, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, true, true>(st, dupi, p.f, w3, p.f, p.cq, p.h, p.f, e3, "dz (up)")));
+          BPT_TRY((gemm<T, true, true>(st, w.dup, p.f, w3, p.f, rows, p.h, p.f, e3, "dz (up)")));
         }
       }
-      float* dh_rows = w.dh + r0 * p.h;
-      BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, h1i, p.h, g2, dyi, p.h, dh_rows,
-                                     w.dh_t + r0 * p.h, p.h, p.cq, dg2, dsh2, w.npart_g,
+      BPT_TRY((norm_bwd<T, float, T>(st, p, w.dz, p.h, h1g, p.h, g2, dyg, p.h, w.dh + g0 * p.h,
+                                     w.dh_t + g0 * p.h, p.h, rows, dg2, dsh2, w.npart_g,
                                      w.npart_b, first, last, &np_n2)));
       // Weight gradients of the group, reduced over all of its rows.
-      if (o + p.cq == grp || last) {
-        const int64_t rows = o + p.cq, g0 = r0 + p.cq - rows;
-        if (dw2) {
-          EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyb + g0 * p.h, p.h, p.f, p.h, rows, e,
-                                         "dW2")));
-        }
-        if (dw1) {
-          EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, rows, e, "dW1")));
-        }
-        if (dw3) {
-          EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, rows, e, "dW3")));
-        }
+      if (dw2) {
+        EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyg, p.h, p.f, p.h, rows, e, "dW2")));
+      }
+      if (dw1) {
+        EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, rows, e, "dW1")));
+      }
+      if (dw3) {
+        EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, rows, e, "dW3")));
       }
     }
     // ---- O-projection backward over the whole sequence: dW_o += O^T dh,
