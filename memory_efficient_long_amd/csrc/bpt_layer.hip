@@ -96,10 +96,10 @@ struct TimedLaunch {
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
 constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
-// The backward runs the FFN recompute and backward on groups of up to this
-// many consecutive query blocks: GEMMs four times taller, a quarter of the
-// launches, and one read-modify-write of the fp32 dW_1 / dW_2 per group. The
-// FFN scratch stays O(c_q f) (no s x f term); the forward keeps one block.
+// Norm2 and the FFN (and in the backward their recompute and gradients) run
+// on groups of up to this many consecutive query blocks: GEMMs four times
+// taller, a quarter of the launches, and one read-modify-write of the fp32
+// dW_1 / dW_2 per group. The FFN scratch stays O(c_q f): no s x f term.
 constexpr int64_t kGradGroupBlocks = 4;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -188,9 +188,11 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
   w.h1 = c.take<float>(p.s * p.h);  // x + attention output projection, whole sequence
-  w.z = c.take<T>(p.cq * p.h);
-  w.u = c.take<T>(p.cq * p.f);
-  w.gate = p.ffn == BPT_SWIGLU ? c.take<T>(p.cq * p.f) : nullptr;
+  // FFN scratch for a group of gq query blocks.
+  const int64_t grp = p.gq * p.cq;
+  w.z = c.take<T>(grp * p.h);
+  w.u = c.take<T>(grp * p.f);
+  w.gate = p.ffn == BPT_SWIGLU ? c.take<T>(grp * p.f) : nullptr;
   return w;
 }
 
@@ -538,20 +540,23 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
       EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
       BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection")));
     }
-    for (int64_t r0 = 0; r0 < p.s; r0 += p.cq) {
-      const float* h1i = w.h1 + r0 * p.h;
-      BPT_TRY((norm_fwd<T, float, T>(st, p, h1i, p.h, g2, sh2, w.z, p.h, p.cq)));
+    // Norm2 and the FFN, a group of gq consecutive query blocks at a time.
+    const int64_t grp = p.gq * p.cq;
+    for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
+      const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
+      const float* h1g = w.h1 + g0 * p.h;
+      BPT_TRY((norm_fwd<T, float, T>(st, p, h1g, p.h, g2, sh2, w.z, p.h, rows)));
       if (p.ffn == BPT_SWIGLU) {
         EpiOut<T, T> eg{w.gate, p.f, b1, 1.f, 0};
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, eg, "ffn gate")));
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, rows, p.f, p.h, eg, "ffn gate")));
         EpiSwiUp<T> eu{w.u, nullptr, w.gate, p.f};
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, p.cq, p.f, p.h, eu, "ffn up")));
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w3, p.f, rows, p.f, p.h, eu, "ffn up")));
       } else {
         EpiAct<T> ea{w.u, nullptr, p.f, b1, act};
-        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, p.cq, p.f, p.h, ea, "ffn fc1")));
+        BPT_TRY((gemm<T, true, false>(st, w.z, p.h, w1, p.f, rows, p.f, p.h, ea, "ffn fc1")));
       }
-      EpiResid<T, float, T> ey{yb + r0 * p.h, p.h, h1i, p.h, b2};
-      BPT_TRY((gemm<T, true, false>(st, w.u, p.f, w2, p.h, p.cq, p.h, p.f, ey, "ffn fc2")));
+      EpiResid<T, float, T> ey{yb + g0 * p.h, p.h, h1g, p.h, b2};
+      BPT_TRY((gemm<T, true, false>(st, w.u, p.f, w2, p.h, rows, p.h, p.f, ey, "ffn fc2")));
     }
   }
   return BPT_OK;
