@@ -357,24 +357,32 @@ bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz
                     int64_t ldo, int64_t rows, float* dg, float* db, float* part_g, float* part_b,
                     int stage, bool finish, int* nparts) {
   if (rows == 0) return BPT_OK;
-  const int nch = (int)((p.h / 8 + 63) / 64);
   const int kind = p.norm == BPT_LAYERNORM ? NORM_LAYER : NORM_RMS;
-  const int nblk = (int)std::min<int64_t>(kNormWaves / 4, (rows + 3) / 4);
+  // Rows of up to 2048 elements: one wave per row; wider rows: the four waves
+  // of a workgroup share a row (a lane then holds at most 32 elements of each
+  // per-row array).
+  const bool wide = p.h > 2048;
+  const int nch = wide ? (int)((p.h / 8 + 255) / 256) : (int)((p.h / 8 + 63) / 64);
+  const int nblk = wide ? (int)std::min<int64_t>(kNormWaves / 4, rows)
+                        : (int)std::min<int64_t>(kNormWaves / 4, (rows + 3) / 4);
   float* pg = dg ? part_g : nullptr;
   float* pb = db ? part_b : nullptr;
   const dim3 grid(nblk), blk(256);
   TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
-#define NB(NC) hipLaunchKernelGGL((norm_bwd_kernel<T, Tin, Tres, NC>), grid, blk, 0, st, dz, lddz, xin, \
-                                  ldx, g, res, ldr, out_f, out_t, ldo, pg, pb, (int)rows, (int)p.h,  \
-                                  kind, p.eps, stage)
-  if (nch <= 1) NB(1); else if (nch <= 2) NB(2); else if (nch <= 4) NB(4);
-  else if (nch <= 8) NB(8); else if (nch <= 16) NB(16); else if (nch <= 32) NB(32);
-  else return fail(BPT_EUNSUPPORTED, "hidden too large for norm kernel");
+#define NB(NC, W) hipLaunchKernelGGL((norm_bwd_kernel<T, Tin, Tres, NC, W>), grid, blk, 0, st, dz, lddz, \
+                                     xin, ldx, g, res, ldr, out_f, out_t, ldo, pg, pb, (int)rows,     \
+                                     (int)p.h, kind, p.eps, stage)
+  if (!wide) {
+    if (nch <= 1) NB(1, 1); else if (nch <= 2) NB(2, 1); else NB(4, 1);
+  } else {
+    if (nch <= 2) NB(2, 4); else if (nch <= 4) NB(4, 4); else if (nch <= 8) NB(8, 4);
+    else return fail(BPT_EUNSUPPORTED, "hidden too large for norm kernel");
+  }
 #undef NB
   BPT_TRY(check_launch("norm_bwd"));
   // The first call of a series writes the most partial rows (it has the most
   // rows); later calls accumulate into a prefix of them.
-  if (stage == 0) *nparts = nblk * 4;
+  if (stage == 0) *nparts = wide ? nblk : nblk * 4;
   if (!finish) return BPT_OK;
   const int P = *nparts;
   const dim3 g2((unsigned)((p.h + 63) / 64));

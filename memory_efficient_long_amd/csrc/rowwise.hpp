@@ -90,19 +90,38 @@ __global__ __launch_bounds__(256) void norm_fwd_kernel(const Tin* __restrict__ x
 
 // Norm backward fused with the residual:
 //   out = res + rstd * (gx - [mean(gx)] - xhat * mean(gx * xhat)),  gx = dz * gamma
-// (the bracketed term only for LayerNorm). Rows are strided over the grid's
-// waves; each wave keeps fp32 partial sums of dz * xhat and dz for the scale
-// and shift gradients and writes them to part_g / part_b [total waves, h].
-template <typename T, typename Tin, typename Tres, int NCH>
+// (the bracketed term only for LayerNorm). A row is handled by WPR waves (one,
+// or all four of the workgroup for wide rows, so that a lane holds at most
+// 8 NCH elements of each per-row array and nothing spills); rows are strided
+// over these units. Each unit keeps fp32 partial sums of dz * xhat and dz for
+// the scale and shift gradients and writes them to part_g / part_b [units, h].
+template <typename T, typename Tin, typename Tres, int NCH, int WPR>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(
     const float* __restrict__ dz, int64_t lddz, const Tin* __restrict__ xin, int64_t ldx,
     const T* __restrict__ gamma, const Tres* __restrict__ res, int64_t ldr, float* out_f,
     T* out_t, int64_t ldo, float* part_g, float* part_b, int rows, int h, int kind, float eps,
     int accumulate_part) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
+  static_assert(WPR == 1 || WPR == 4, "waves per row");
+  constexpr int CW = 64 * WPR;  // chunk stride of a unit
+  const int lane = (WPR == 1 ? threadIdx.x & 63 : threadIdx.x);
+  const int wid = threadIdx.x >> 6;
+  const int wave = WPR == 1 ? blockIdx.x * 4 + wid : blockIdx.x;  // unit index
+  const int nwaves = WPR == 1 ? gridDim.x * 4 : gridDim.x;
   const int nch = h / 8;
+  __shared__ float red[2][4];
+  // Sum over the unit (two values at once); WPR = 4 exchanges the per-wave
+  // sums through LDS, with barriers on both sides so the slots can be reused.
+  auto unit_sum2 = [&](float& a, float& b) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if constexpr (WPR == 4) {
+      if ((threadIdx.x & 63) == 0) { red[0][wid] = a; red[1][wid] = b; }
+      __syncthreads();
+      a = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+      b = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+      __syncthreads();
+    }
+  };
   const float inv_h = 1.f / (float)h;
   float pg[NCH][8], pb[NCH][8];
 #pragma unroll
@@ -115,29 +134,33 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
+      const int c = lane + CW * i;
       if (c < nch) {
         load8(xin + (int64_t)row * ldx + 8 * c, xv[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum += xv[i][e];
       }
     }
-    float mean = 0.f;
-    if (kind == NORM_LAYER) mean = wave_sum(sum) * inv_h;
+    float mean = 0.f, dummy = 0.f;
+    if (kind == NORM_LAYER) {
+      unit_sum2(sum, dummy);
+      mean = sum * inv_h;
+    }
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
-      if (lane + 64 * i < nch)
+      if (lane + CW * i < nch)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float d = xv[i][e] - mean;
           sq += d * d;
         }
-    const float rstd = 1.f / sqrtf(wave_sum(sq) * inv_h + eps);
+    unit_sum2(sq, dummy);
+    const float rstd = 1.f / sqrtf(sq * inv_h + eps);
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
+      const int c = lane + CW * i;
       if (c < nch) {
         float dzv[8];
         load8(dz + (int64_t)row * lddz + 8 * c, dzv);
@@ -154,11 +177,12 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
         }
       }
     }
-    const float m1 = kind == NORM_LAYER ? wave_sum(s1) * inv_h : 0.f;
-    const float m2 = wave_sum(s2) * inv_h;
+    unit_sum2(s1, s2);
+    const float m1 = kind == NORM_LAYER ? s1 * inv_h : 0.f;
+    const float m2 = s2 * inv_h;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
+      const int c = lane + CW * i;
       if (c < nch) {
         float rv[8], o[8];
         load8(res + (int64_t)row * ldr + 8 * c, rv);
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = lane + 64 * i;
+    const int c = lane + CW * i;
     if (c < nch) {
       if (accumulate_part) {  // running partials over several calls
         float og[8], ob[8];

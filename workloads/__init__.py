@@ -116,6 +116,10 @@ SMALL: Dict[str, LayerShape] = {
     "gpt1b-small-5blocks": WORKLOADS["gpt1b-s8k"].replace(
         name="gpt1b-small-5blocks", seq_len=640, hidden=256, n_heads=2, n_kv_heads=2,
         ffn_dim=512, q_block=128, kv_block=320, head_chunk=2),
+    # Hidden 4096: the norm backward shares each row among a workgroup's waves.
+    "bf16-wide-rows": WORKLOADS["llama8b-s64k"].replace(
+        name="bf16-wide-rows", seq_len=144, hidden=4096, n_heads=32, n_kv_heads=8,
+        ffn_dim=512, q_block=48, kv_block=144, head_chunk=32),
     "bf16-d64-noncausal": WORKLOADS["gpt1b-s8k"].replace(
         name="bf16-d64-noncausal", seq_len=336, hidden=256, n_heads=4, n_kv_heads=4,
         head_dim=64, ffn_dim=512, causal=False, q_block=112, kv_block=168, head_chunk=4),
