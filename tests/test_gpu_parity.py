@@ -105,6 +105,39 @@ def test_no_writes_outside_outputs_and_reproducible():
     assert torch.equal(y1, y2)
 
 
+def test_batch_and_gradient_accumulation():
+    """Two independent sequences in one call match the oracle (which sums the
+    parameter gradients over the batch); a second backward with accumulate=1
+    adds the same gradients onto the first call's (fp32, so twice the value
+    up to rounding), and dx is unaffected by accumulate."""
+    import memory_efficient_long_amd as bpt
+    from harness import to_device
+    sh = wl.SMALL["gpt1b-small"].replace(name="gpt1b-small-b2", batch=2, seq_len=400,
+                                          q_block=200, kv_block=400)
+    _say(f"[batch] {sh.name} b={sh.batch} s={sh.seq_len}")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    gpu = run_gpu(inp)
+    errs = compare(gpu, run_oracle(inp), sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
+    _say(f"  errs {errs}")
+    _check(errs, sh.dtype)
+
+    cfg = bpt.LayerConfig.from_shape(sh)
+    x = to_device(inp.x)
+    w = {k: to_device(v) for k, v in inp.w.items()}
+    dy = to_device(inp.dy)
+    _, saved = bpt.forward(cfg, x, w)
+    dx1, g1 = bpt.backward(cfg, x, w, saved, dy)
+    g1 = {k: v.clone() for k, v in g1.items()}
+    grads = {k: v.clone() for k, v in g1.items()}
+    dx2, g2 = bpt.backward(cfg, x, w, saved, dy, grads=grads, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2)
+    for k in g1:
+        ref = 2.0 * g1[k].double()
+        err = (g2[k].double() - ref).norm() / max(ref.norm(), 1e-30)
+        assert err < 1e-6, (k, float(err))
+
+
 # ----------------------------------------------------------------- full-size workloads
 FULL = ["gpt-tiny-fp32", "gpt1b-s8k", "gpt1b-s128k", "llama8b-s64k", "llama70b-s8k"]
 
