@@ -358,11 +358,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     vf[c] = kvrow < s ? ld_frag(Vp + (int64_t)kvrow * D + 16 * c + 8 * g) : zero_frag<bf16>();
   }
   // The last KPARK K fragments are parked in LDS and read back where they are
-  // used: the registers they free keep the loop free of spills, whose reloads
-  // (counted with the direct loads by vmcnt) would wait for the tile loads.
-  // Two measured best (8 KiB per workgroup; four would leave room for only one
-  // workgroup per CU).
-  constexpr int KPARK = 2;
+  // used: the registers they free keep the loop free of spills (whose reloads,
+  // counted with the direct loads by vmcnt, would wait for the tile loads) and
+  // leave room to read fragments ahead of their MFMAs. Three measured best
+  // (12 KiB per workgroup; four would leave room for only one workgroup per CU).
+  constexpr int KPARK = 3;
   __shared__ __attribute__((aligned(16))) bf16x8 kpark[KPARK > 0 ? KPARK : 1][4][64];
 #pragma unroll
   for (int c = 0; c < KPARK; ++c) kpark[c][w][lane] = kf[NC - KPARK + c];
@@ -445,6 +445,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         sacc = mma(TL::frag_at(qsa + buf * TB, rf, qb, c), kc, sacc);
         dpacc = mma(TL::frag_at(dosa + buf * TB, rf, qb, c), vf[c], dpacc);
       }
+      // Order hint (sched_group_barrier; 0x100 = LDS reads, 0x008 = MFMA): the
+      // eight statistics reads and the first PF fragment reads, then each MFMA
+      // followed by the next fragment read, so a read is issued PF MFMAs before
+      // its use instead of right before it.
+      {
+        constexpr int PF = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 + PF, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * NC - PF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(sacc[r] * sl2);
@@ -476,6 +490,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
           dvacc[i] = mma(pa, TL::tr_at(dosa + buf * TB, trb, cc, i), dvacc[i]);
           dkacc[i] = mma(dsa, TL::tr_at(qsa + buf * TB, trb, cc, i), dkacc[i]);
         }
+      }
+      // Same for dV and dK: two transpose reads per MFMA.
+      {
+        constexpr int PF = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int m = 0; m < 4 * ND - PF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
       }
     }
     if (step + 1 < nsteps) store_stats(buf ^ 1);
