@@ -39,64 +39,22 @@ struct DmaTile {
   __device__ static __forceinline__ int f(int r) {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
-  __device__ static __forceinline__ int off(int r, int chunk) {
-    return r * RB + ((chunk ^ f(r)) << 4);
-  }
-
-  // Issue the direct loads of rows [row0, row0 + R) of src (row stride ld
-  // elements) into tile; rows at or past rlim repeat row rlim - 1 (they are
-  // masked by the caller). NW waves share the tile.
-  template <int R, int NW>
-  __device__ static __forceinline__ void load(bf16* tile, const bf16* src, int64_t ld, int row0,
-                                              int rlim, int w, int lane) {
-    constexpr int PERW = R * RB / 1024 / NW;
-    static_assert(PERW >= 1 && R * RB % (1024 * NW) == 0, "tile split");
-#pragma unroll
-    for (int m = 0; m < PERW; ++m) {
-      const int base = (w * PERW + m) * 1024;
-      const int o = base + 16 * lane;
-      const int r = o / RB, p = (o % RB) >> 4;
-      const int gr = min(row0 + r, rlim - 1);
-      const bf16* gp = src + (int64_t)gr * ld + ((p ^ f(r)) << 3);
-      dma16_v(gp, lds_addr((const char*)tile + base));
-    }
-  }
-
-  // Elements [k0, k0 + 8) of row r (k0 % 8 == 0).
-  __device__ static __forceinline__ bf16x8 frag(const bf16* tile, int r, int k0) {
-    return ld<bf16x8>((const char*)tile + off(r, k0 >> 3));
-  }
-
-  // Transposed-operand fragment for output column n = 32 i + (lane % 32) and
-  // reduction chunk cc: elements 0-3 = rows 16cc + 4g + {0..3}, elements 4-7 =
-  // rows 16cc + 8 + 4g + {0..3} (g = lane / 32), all at column n.
-  __device__ static __forceinline__ bf16x8 tr_frag(const bf16* tile, int cc, int i, int lane) {
-    const int li = lane & 15, g = lane >> 5;
-    const int col = 32 * i + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-    const int r0 = 16 * cc + 4 * g + (li >> 2);
-    const int pc = ((col >> 3) ^ f(r0)) << 4;
-    const int pb = ((col >> 2) & 1) << 3;
-    // Tiles are 1024-byte aligned and rows RB-aligned, so XOR-ing the byte
-    // address by 32 flips bit 1 of the chunk index: f(r0 + 8) = f(r0) ^ 2.
-    const uint32_t a0 = (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)tile) +
-                        r0 * RB + pc + pb;
-    const uint32_t a1 = (a0 ^ 32u) + 8 * RB;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(size_t)a0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(size_t)a1);
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-  }
-
-  // ---- Fragment reads from a per-lane constant base: the chunk permutation
-  // is an XOR on bits that lie below the row stride, so every fragment of a
-  // lane is its base XOR a compile-time constant plus a constant offset (one
-  // base register per read form instead of one address per fragment).
+  // Tile layout: row r (RB bytes) holds its 16-byte chunk c at byte
+  // r RB + 16 (c ^ f(r)). Tiles are 1024-byte aligned.
+  //
+  // Fragment reads from a per-lane constant base: the chunk permutation is an
+  // XOR on bits that lie below the row stride, so every fragment of a lane is
+  // its base XOR a compile-time constant plus a constant offset (one base
+  // register per read form instead of one address per fragment).
   //   row fragment (row 32 blk + lane % 32, elements 16 c + 8 g .. + 7):
   //     tile + 32 blk RB + (rf ^ 32 c)
-  //   transpose fragment (as tr_frag(cc, i)):
+  //   transposed-operand fragment for output column n = 32 i + lane % 32 and
+  //   reduction chunk cc (elements 0-3 = rows 16 cc + 4 g + {0..3}, elements
+  //   4-7 = rows 16 cc + 8 + 4 g + {0..3}, all at column n), two 8-byte
+  //   transpose reads:
   //     a0 = tile + 16 cc RB + (tr ^ 64 i), a1 = (a0 ^ 32) + 8 RB
+  //   (XOR-ing the byte address by 32 flips bit 1 of the chunk index, and
+  //   f(r + 8) = f(r) ^ 2).
   __device__ static __forceinline__ uint32_t rf_base(int lane) {
     const int lr = lane & 31, g = lane >> 5, F = f(lr);
     return lr * RB + 32 * (F >> 1) + 16 * (g ^ (F & 1));
