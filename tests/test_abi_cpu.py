@@ -186,3 +186,15 @@ def test_weight_set_matches_printed_parameter_counts(repo_root):
                                                head_dim=min(128, h), ffn_dim=4 * h)
         n = sum(int(__import__("numpy").prod(s)) for s in wl.weight_shapes(sh).values())
         assert n == count == 12 * h * h + 13 * h
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark is single-GPU: asking for more exits non-zero with a
+    message instead of running (and reporting) anything."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode != 0
+    assert "one GPU" in proc.stderr
+    assert proc.stdout.strip() == ""
