@@ -100,6 +100,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt1b-s128k")
+    ap.add_argument("--head-chunk", type=int, default=0, metavar="U",
+                    help="query heads per attention stage (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
     ap.add_argument("--breakdown", action="store_true",
@@ -132,6 +134,8 @@ def main() -> int:
 
     bpt.load_library()
     sh = wl.WORKLOADS[args.workload]
+    if args.head_chunk:
+        sh = sh.replace(head_chunk=args.head_chunk)
     cfg = bpt.LayerConfig.from_shape(sh)
     desc = cfg.desc()
     dev = torch.device("cuda:0")
@@ -219,7 +223,10 @@ def main() -> int:
     kernel_name = dom + ("_dma_kernel" if dma else "_kernel")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": load_traffic(kernel_name, sh.name), "kernel": kernel_name,
+                # counters are taken at the workload's own head chunk
+                "traffic": (load_traffic(kernel_name, sh.name)
+                            if sh.head_chunk == wl.WORKLOADS[args.workload].head_chunk else None),
+                "kernel": kernel_name,
                 "avg_launch_ms": round(avg_ms, 3), "launches_per_step": dom_n / args.steps,
                 "algorithmic_flops_per_launch": per_launch_flops,
                 "hardware_flops_per_launch": fl["hw_" + dom] / max(dom_n / args.steps, 1)}

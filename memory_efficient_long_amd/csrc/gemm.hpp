@@ -59,6 +59,13 @@ __device__ __forceinline__ float sigmoidf_(float a) {
 
 enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
 
+// Value of lane ^ 1 (the neighbouring accumulator column): a DPP quad
+// permutation [1, 0, 3, 2], a single VALU move.
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
 // ----------------------------------------------------------------- epilogues
 // Each epilogue is applied to one 32 x 32 accumulator block of a lane (one
 // column, 16 rows) in three steps: col(n) loads what depends on the column
@@ -89,53 +96,83 @@ struct EpiOut {
 };
 
 // Q/K/V projection: + bias, optional RoPE on interleaved pairs, scattered to a
-// head-major [heads, s, D] buffer.
+// head-major [heads, s, D] buffer. Everything that depends on the column only
+// (bias, destination head and offset, rotation role) is resolved once per
+// lane in col(); each element then costs one row offset and a store.
 template <typename T>
 struct EpiQKV {
   T* out; int64_t head_stride; int D; const T* bias; const float2* rope; int row0;
   static constexpr bool kPair = true;
-  struct Col { float b, bp; };
+  struct Col { float b, bp; T* dst; int rc, rot; };  // rot: 0 none, 1 even, 2 odd member
   struct Pre { float2 cs; };
   __device__ __forceinline__ Col col(int n) const {
-    return bias ? Col{to_f32(bias[n]), to_f32(bias[n ^ 1])} : Col{0.f, 0.f};
-  }
-  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
-    if (!rope) return {{1.f, 0.f}};
-    return {rope[(int64_t)(row0 + m) * (D / 2) + ((n % D) >> 1)]};
-  }
-  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Col& c,
-                                        const Pre& p) const {
-    v += c.b; vp += c.bp;
     const int head = n / D, dd = n - head * D;
-    if (rope) v = (dd & 1) ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
-    out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
+    Col c;
+    c.b = bias ? to_f32(bias[n]) : 0.f;
+    c.bp = bias ? to_f32(bias[n ^ 1]) : 0.f;
+    c.dst = out + (int64_t)head * head_stride + dd;
+    c.rc = dd >> 1;
+    c.rot = rope ? 1 + (dd & 1) : 0;
+    return c;
+  }
+  // Branches only on `rope` (uniform across the wave); the per-lane role
+  // is applied with selects.
+  __device__ __forceinline__ bool paired() const { return rope != nullptr; }
+  __device__ __forceinline__ Pre pre(int m, int, const Col& c) const {
+    if (!rope) return {{1.f, 0.f}};
+    return {rope[(int64_t)(row0 + m) * (D / 2) + c.rc]};
+  }
+  __device__ __forceinline__ void apply(int m, int, float v, float vp, const Col& c,
+                                        const Pre& p) const {
+    v += c.b;
+    if (rope) {
+      vp += c.bp;
+      const float r = c.rot == 2 ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
+      v = c.rot ? r : v;
+    }
+    c.dst[(int64_t)m * D] = from_f32<T>(v);
   }
 };
 
 // Q, K and V projections of all heads in one GEMM (columns [0, c1) -> q,
 // [c1, c2) -> k, [c2, N) -> v; c1, c2 multiples of D): + bias, RoPE on the
-// q and k columns, scattered to head-major [heads, s, D] buffers.
+// q and k columns, scattered to head-major [heads, s, D] buffers. Column-only
+// work is resolved in col(), as in EpiQKV.
 template <typename T>
 struct EpiQKV3 {
   T* q; T* k; T* v; int64_t head_stride; int D; const T* bias; const float2* rope; int c1, c2;
   static constexpr bool kPair = true;
-  struct Col { float b, bp; };
+  struct Col { float b, bp; T* dst; int rc, rot; };
   struct Pre { float2 cs; };
   __device__ __forceinline__ Col col(int n) const {
-    return bias ? Col{to_f32(bias[n]), to_f32(bias[n ^ 1])} : Col{0.f, 0.f};
-  }
-  __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
-    if (!rope || n >= c2) return {{1.f, 0.f}};
-    return {rope[(int64_t)m * (D / 2) + ((n % D) >> 1)]};
-  }
-  __device__ __forceinline__ void apply(int m, int n, float v, float vp, const Col& c,
-                                        const Pre& p) const {
-    v += c.b; vp += c.bp;
-    T* out = n < c1 ? q : (n < c2 ? k : this->v);
+    T* base = n < c1 ? q : (n < c2 ? k : this->v);
     const int nn = n < c1 ? n : (n < c2 ? n - c1 : n - c2);
     const int head = nn / D, dd = nn - head * D;
-    if (rope && n < c2) v = (dd & 1) ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
-    out[(int64_t)head * head_stride + (int64_t)m * D + dd] = from_f32<T>(v);
+    Col c;
+    c.b = bias ? to_f32(bias[n]) : 0.f;
+    c.bp = bias ? to_f32(bias[n ^ 1]) : 0.f;
+    c.dst = base + (int64_t)head * head_stride + dd;
+    c.rc = dd >> 1;
+    c.rot = rope && n < c2 ? 1 + (dd & 1) : 0;
+    return c;
+  }
+  __device__ __forceinline__ bool paired() const { return rope != nullptr; }
+  // The rotation entry is loaded for every column when RoPE is on (v columns
+  // ignore it): the address is valid for any column, and no per-lane branch
+  // guards the load.
+  __device__ __forceinline__ Pre pre(int m, int, const Col& c) const {
+    if (!rope) return {{1.f, 0.f}};
+    return {rope[(int64_t)m * (D / 2) + c.rc]};
+  }
+  __device__ __forceinline__ void apply(int m, int, float val, float vp, const Col& c,
+                                        const Pre& p) const {
+    val += c.b;
+    if (rope) {
+      vp += c.bp;
+      const float r = c.rot == 2 ? (vp * p.cs.y + val * p.cs.x) : (val * p.cs.x - vp * p.cs.y);
+      val = c.rot ? r : val;
+    }
+    c.dst[(int64_t)m * D] = from_f32<T>(val);
   }
 };
 
@@ -252,7 +289,7 @@ __device__ __forceinline__ void epilogue_block(const Epi& epi, const f32x16& acc
     const int row = m0 + acc_row(r, g);
     const float v = acc[r];
     float vp = 0.f;
-    if constexpr (Epi::kPair) vp = shfl_xor(v, 1);
+    if constexpr (Epi::kPair) vp = epi.paired() ? lane_xor1(v) : 0.f;
     if (EVEN || (row < M && col < N)) epi.apply(row, col, v, vp, cv, pre[r]);
   }
 }
