@@ -400,7 +400,12 @@ bpt_status colsum(hipStream_t st, const Tin* X, int64_t ldx, int64_t rows, int64
   if (!out || N == 0) return BPT_OK;
   int P = (int)std::min<int64_t>(kColsumParts, rows);
   TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
-  if (rows > 0)
+  constexpr int V = 16 / (int)sizeof(Tin);
+  const bool vec = (uintptr_t)X % 16 == 0 && N % V == 0 && ldx % V == 0;
+  if (rows > 0 && vec)
+    hipLaunchKernelGGL(colsum_partial_vec_kernel<Tin>, dim3((unsigned)((N + 64 * V - 1) / (64 * V)), P),
+                       dim3(256), 0, st, X, ldx, (int)rows, (int)N, part, stage);
+  else if (rows > 0)
     hipLaunchKernelGGL(colsum_partial_kernel<Tin>, dim3((unsigned)((N + 63) / 64), P), dim3(256), 0,
                        st, X, ldx, (int)rows, (int)N, part, stage);
   if (nparts) {
@@ -693,8 +698,17 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     // ---- attention backward per head chunk
     {
     TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
-    hipLaunchKernelGGL(attn_dvec_kernel<T>, dim3((unsigned)((p.s * p.H + 255) / 256)), dim3(256),
-                       0, st, w.dO, Ob, HD, w.dvec, (int)p.s, (int)p.H, (int)p.D);
+    // D / 8 lanes per (row, head); D is 32, 64 or 128 (validated)
+    const dim3 gd((unsigned)((p.s * p.H * (p.D / 8) + 255) / 256));
+    if (p.D == 128)
+      hipLaunchKernelGGL((attn_dvec_kernel<T, 16>), gd, dim3(256), 0, st, w.dO, Ob, HD, w.dvec,
+                         (int)p.s, (int)p.H);
+    else if (p.D == 64)
+      hipLaunchKernelGGL((attn_dvec_kernel<T, 8>), gd, dim3(256), 0, st, w.dO, Ob, HD, w.dvec,
+                         (int)p.s, (int)p.H);
+    else
+      hipLaunchKernelGGL((attn_dvec_kernel<T, 4>), gd, dim3(256), 0, st, w.dO, Ob, HD, w.dvec,
+                         (int)p.s, (int)p.H);
     BPT_TRY(check_launch("attn_dvec"));
     }
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {

@@ -72,15 +72,28 @@ __global__ __launch_bounds__(256) void norm_fwd_kernel(const Tin* __restrict__ x
         sq += d * d;
       }
   const float rstd = 1.f / sqrtf(wave_sum(sq) * inv_h + eps);
+  // gamma / beta need only element alignment; 16-byte aligned ones (the
+  // usual case, a uniform test) are read as vectors.
+  const bool gvec = (((uintptr_t)gamma | (uintptr_t)beta) & 15) == 0;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
-      float o[8];
+      float gm[8], bt[8], o[8];
+      if (gvec) {
+        load8(gamma + 8 * c, gm);
+        if (beta) load8(beta + 8 * c, bt);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          gm[e] = to_f32(gamma[8 * c + e]);
+          if (beta) bt[e] = to_f32(beta[8 * c + e]);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float y = (v[i][e] - mean) * rstd * to_f32(gamma[8 * c + e]);
-        if (beta) y += to_f32(beta[8 * c + e]);
+        float y = (v[i][e] - mean) * rstd * gm[e];
+        if (beta) y += bt[e];
         o[e] = y;
       }
       store8(out + (int64_t)row * ldo + 8 * c, o);
@@ -123,6 +136,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     }
   };
   const float inv_h = 1.f / (float)h;
+  const bool gvec = ((uintptr_t)gamma & 15) == 0;  // uniform: vector reads of gamma
   float pg[NCH][8], pb[NCH][8];
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
@@ -162,13 +176,19 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + CW * i;
       if (c < nch) {
-        float dzv[8];
+        float dzv[8], gm[8];
         load8(dz + (int64_t)row * lddz + 8 * c, dzv);
+        if (gvec) {
+          load8(gamma + 8 * c, gm);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gm[e] = to_f32(gamma[8 * c + e]);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xh = (xv[i][e] - mean) * rstd;
           xv[i][e] = xh;
-          const float gx = dzv[e] * to_f32(gamma[8 * c + e]);
+          const float gx = dzv[e] * gm[e];
           gv[i][e] = gx;
           s1 += gx;
           s2 += gx * xh;
@@ -239,6 +259,57 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restri
   }
 }
 
+// Stage 1 with 16-byte loads (X 16-byte aligned, N and ldx multiples of the
+// vector width V): each thread sums V adjacent columns, so a wave reads 1 KiB
+// of a row per load; rows are taken four at a time per lane to keep several
+// loads in flight. Same grid semantics as above with 64 V columns per block.
+template <typename Tin>
+__global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __restrict__ X,
+                                                                 int64_t ldx, int rows, int N,
+                                                                 float* part, int accumulate) {
+  constexpr int V = 16 / (int)sizeof(Tin);
+  struct Elems { Tin e[V]; };
+  __shared__ float red[4][64 * V];
+  const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int c0 = (blockIdx.x * 64 + cl) * V;
+  const int per = (rows + gridDim.y - 1) / gridDim.y;
+  const int r0 = blockIdx.y * per, r1 = min(rows, r0 + per);
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.f;
+  if (c0 < N) {
+    const Tin* base = X + c0;
+    int r = r0 + rl;
+    for (; r + 12 < r1; r += 16) {
+      u32x4 u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = *(const u32x4*)(base + (int64_t)(r + 4 * i) * ldx);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const Elems x = __builtin_bit_cast(Elems, u[i]);
+#pragma unroll
+        for (int j = 0; j < V; ++j) acc[j] += to_f32(x.e[j]);
+      }
+    }
+    for (; r < r1; r += 4) {
+      const Elems x = __builtin_bit_cast(Elems, *(const u32x4*)(base + (int64_t)r * ldx));
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] += to_f32(x.e[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) red[rl][cl * V + j] = acc[j];
+  __syncthreads();
+  for (int c = threadIdx.x; c < 64 * V; c += 256) {
+    const int col = blockIdx.x * 64 * V + c;
+    if (col < N) {
+      const float v = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+      float* o = part + (int64_t)blockIdx.y * N + col;
+      *o = accumulate ? *o + v : v;
+    }
+  }
+}
+
 // Stage 2: out[col] (+)= sum_p part[p, col]; block = 64 columns x 4 partial
 // lanes, each lane summing every 4th partial row, then an LDS reduction.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int P,
@@ -279,25 +350,33 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* tab, int s, int
   tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// D[h, q] = sum_d dO[q, h D + d] * O[q, h D + d] (fp32), one thread per (row, head).
-template <typename T>
+// D[h, q] = sum_d dO[q, h D + d] * O[q, h D + d] (fp32). The L = D / 8 lanes
+// of one (row, head) pair each read an 8-element piece, side by side, so a
+// wave reads 64 / L consecutive pairs of a row as one contiguous span; the
+// pieces are then summed across the L lanes with xor shuffles.
+template <typename T, int L>
 __global__ __launch_bounds__(256) void attn_dvec_kernel(const T* __restrict__ dout,
                                                         const T* __restrict__ o, int64_t ld,
-                                                        float* dvec, int s, int nh, int D) {
+                                                        float* dvec, int s, int nh) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)s * nh) return;
-  const int row = (int)(t / nh), h = (int)(t % nh);
-  const T* a = dout + (int64_t)row * ld + (int64_t)h * D;
-  const T* b = o + (int64_t)row * ld + (int64_t)h * D;
+  const int64_t pair = t / L;
+  const int piece = (int)(t % L);
+  const bool ok = pair < (int64_t)s * nh;
+  int row = 0, h = 0;
   float acc = 0.f;
-  for (int c = 0; c < D; c += 8) {
+  if (ok) {
+    row = (int)(pair / nh);
+    h = (int)(pair - (int64_t)row * nh);
+    const int64_t off = (int64_t)row * ld + (int64_t)h * (8 * L) + 8 * piece;
     float va[8], vb[8];
-    load8(a + c, va);
-    load8(b + c, vb);
+    load8(dout + off, va);
+    load8(o + off, vb);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += va[e] * vb[e];
   }
-  dvec[(int64_t)h * s + row] = acc;
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+  if (ok && piece == 0) dvec[(int64_t)h * s + row] = acc;
 }
 
 }  // namespace bpt
