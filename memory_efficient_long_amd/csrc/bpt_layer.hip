@@ -174,7 +174,7 @@ struct Carver {
 
 template <typename T>
 struct FwdWs {
-  T *xn, *q, *k, *v, *z, *u, *gate;
+  T *xn, *q, *k, *v, *z, *u, *gate, *wc, *bc;
   float* h1;
   float2* rope;
 };
@@ -187,6 +187,10 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
   w.q = c.take<T>(p.U * p.s * p.D);
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
+  if (p.U < p.H) {  // a head chunk's Q|K|V weight columns (and biases), gathered
+    w.wc = c.take<T>(p.h * p.chunk_cols);
+    w.bc = c.take<T>(p.chunk_cols);
+  }
   w.h1 = c.take<float>(p.s * p.h);  // x + attention output projection, whole sequence
   // FFN scratch for a group of gq query blocks.
   const int64_t grp = p.gq * p.cq;
@@ -198,7 +202,7 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
 
 template <typename T>
 struct BwdWs {
-  T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t;
+  T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t, *wc, *bc;
   float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b;
   float2* rope;
 };
@@ -217,6 +221,10 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.k = c.take<T>(p.nkvc * p.s * p.D);
   w.v = c.take<T>(p.nkvc * p.s * p.D);
   w.dqkv = c.take<T>(p.s * p.chunk_cols);
+  if (p.U < p.H) {
+    w.wc = c.take<T>(p.h * p.chunk_cols);
+    w.bc = c.take<T>(p.chunk_cols);
+  }
   w.h1 = c.take<float>(p.s * p.h);  // recomputed x + O W_o + b_o, whole sequence
   // FFN activations and gradients for a group of gq query blocks.
   const int64_t grp = p.gq * p.cq;
@@ -494,27 +502,49 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   return check_launch("attn_bwd_dq");
 }
 
-// Q, K, V of head chunk c (query heads [c U, (c+1) U)) into head-major buffers.
+// Column offsets in W_qkv of head chunk c's Q, K and V parts.
+struct ChunkCols {
+  int64_t off[3], width[3];
+};
+inline ChunkCols chunk_cols_of(const Plan& p, int64_t c) {
+  const int64_t hq0 = c * p.U, hk0 = hq0 / p.G;
+  return {{hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D},
+          {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D}};
+}
+
+// Q, K, V of head chunk c (query heads [c U, (c+1) U)) into head-major
+// buffers. With several chunks, the chunk's weight columns (and biases) are
+// first gathered into one contiguous [h, chunk_cols] block wc (bc), so the
+// projection is a single GEMM; the backward reuses wc for dxn.
 template <typename T>
 bpt_status qkv_chunk(hipStream_t st, const Plan& p, const T* xn, const T* wqkv, const T* bqkv,
-                     int64_t c, T* q, T* k, T* v, const float2* rope) {
-  const int64_t hq0 = c * p.U, hk0 = hq0 / p.G;
-  const int64_t cols[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
-  const int64_t widths[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};
+                     int64_t c, T* q, T* k, T* v, const float2* rope, T* wc, T* bc) {
+  const int c1 = (int)(p.U * p.D), c2 = (int)((p.U + p.nkvc) * p.D);
   if (p.U == p.H) {  // all heads in one chunk: one GEMM over the packed Q|K|V columns
-    EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv, rope, (int)(p.H * p.D),
-                 (int)((p.H + p.Hkv) * p.D)};
+    EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv, rope, c1, c2};
     BPT_TRY((gemm<T, true, false>(st, xn, p.h, wqkv, p.qkv_cols, p.s, p.qkv_cols, p.h, e,
                                   "qkv projection")));
     return BPT_OK;
   }
-  T* outs[3] = {q, k, v};
-  for (int part = 0; part < 3; ++part) {
-    EpiQKV<T> e{outs[part], p.s * p.D, (int)p.D, bqkv ? bqkv + cols[part] : nullptr,
-                part < 2 ? rope : nullptr, 0};
-    BPT_TRY((gemm<T, true, false>(st, xn, p.h, wqkv + cols[part], p.qkv_cols, p.s, widths[part],
-                                  p.h, e, "qkv projection")));
+  const ChunkCols cc = chunk_cols_of(p, c);
+  {
+    constexpr int V = 16 / (int)sizeof(T);
+    TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+    const int64_t nv = p.h * p.chunk_cols / V;
+    // W_qkv is 16-byte aligned with rows and head columns of 16-byte
+    // multiples; the bias is only element-aligned, so it is copied per element.
+    hipLaunchKernelGGL((gather_cols3_kernel<T, V>), dim3((unsigned)((nv + 255) / 256)), dim3(256),
+                       0, st, wqkv, p.qkv_cols, wc, (int)p.h, c1, c2, (int)p.chunk_cols,
+                       cc.off[0], cc.off[1], cc.off[2]);
+    if (bqkv)
+      hipLaunchKernelGGL((gather_cols3_kernel<T, 1>), dim3((unsigned)((p.chunk_cols + 255) / 256)),
+                         dim3(256), 0, st, bqkv, p.qkv_cols, bc, 1, c1, c2, (int)p.chunk_cols,
+                         cc.off[0], cc.off[1], cc.off[2]);
+    BPT_TRY(check_launch("gather qkv chunk"));
   }
+  EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv ? bc : nullptr, rope, c1, c2};
+  BPT_TRY((gemm<T, true, false>(st, xn, p.h, wc, p.chunk_cols, p.s, p.chunk_cols, p.h, e,
+                                "qkv projection (chunk)")));
   return BPT_OK;
 }
 
@@ -544,7 +574,7 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
     float* Lb = LSE + bi * p.H * p.s;
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
-      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
+      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
       BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s));
     }
     // Output projection + residual for the whole sequence in one GEMM (it is
@@ -713,7 +743,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     }
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
       const int64_t hq0 = ch * p.U, hk0 = hq0 / p.G;
-      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope));
+      BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
       T* dK = w.dqkv + p.U * p.D;
       T* dV = w.dqkv + (p.U + p.nkvc) * p.D;
       BPT_TRY(attn_bwd<T>(st, p, w.q, w.k, w.v, w.dO + hq0 * p.D, Lb + hq0 * p.s,
@@ -735,19 +765,23 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
                                      p.qkv_cols, e, "dxn")));
         continue;
       }
-      for (int seg = 0; seg < 3; ++seg) {
-        const T* dseg = w.dqkv + segc[seg];
-        if (dwqkv) {
-          EpiOut<T, float> e{dwqkv + wcol[seg], p.qkv_cols, nullptr, 1.f, 1};
-          BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, dseg, p.chunk_cols, p.h, wid[seg], p.s, e,
-                                         "dWqkv")));
-        }
-        BPT_TRY(colsum<T>(st, dseg, p.chunk_cols, p.s, wid[seg], w.part,
-                          dbqkv ? dbqkv + wcol[seg] : nullptr));
-        EpiOut<T, float> e{w.dxn, p.h, nullptr, 1.f, (ch == 0 && seg == 0) ? 0 : 1};
-        BPT_TRY((gemm<T, true, true>(st, dseg, p.chunk_cols, wqkv + wcol[seg], p.qkv_cols, p.s, p.h,
-                                     wid[seg], e, "dxn")));
+      // Several chunks: dQ|dK|dV of the chunk are contiguous in dqkv, so the
+      // weight gradient is one GEMM whose epilogue scatters the three column
+      // segments to their places in dW_qkv, and dxn is one GEMM against the
+      // gathered weight columns wc (from qkv_chunk above).
+      const ChunkCols cc = chunk_cols_of(p, ch);
+      if (dwqkv) {
+        EpiOut3<T> e{dwqkv + cc.off[0], dwqkv + cc.off[1], dwqkv + cc.off[2], p.qkv_cols,
+                     (int)segc[1], (int)segc[2], 1};
+        BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, w.dqkv, p.chunk_cols, p.h, p.chunk_cols,
+                                       p.s, e, "dWqkv (chunk)")));
       }
+      for (int seg = 0; seg < 3; ++seg)
+        BPT_TRY(colsum<T>(st, w.dqkv + segc[seg], p.chunk_cols, p.s, wid[seg], w.part,
+                          dbqkv ? dbqkv + wcol[seg] : nullptr));
+      EpiOut<T, float> e{w.dxn, p.h, nullptr, 1.f, ch == 0 ? 0 : 1};
+      BPT_TRY((gemm<T, true, true>(st, w.dqkv, p.chunk_cols, w.wc, p.chunk_cols, p.s, p.h,
+                                   p.chunk_cols, e, "dxn (chunk)")));
     }
     // ---- Norm1 backward + residual: dx = dh + Norm1'(dxn)
     int np_n1 = 0;

@@ -95,6 +95,28 @@ struct EpiOut {
   }
 };
 
+// out_k[m, n - start_k] (+)= v for the three column segments [0, c1),
+// [c1, c2), [c2, N) (start_k = 0, c1, c2) of the product, each written into
+// its own column range of an fp32 matrix with row stride ldo: the weight
+// gradient of a head chunk, whose Q, K and V columns are apart in W_qkv.
+template <typename T>
+struct EpiOut3 {
+  float* out0; float* out1; float* out2; int64_t ldo; int c1, c2; int accumulate;
+  static constexpr bool kPair = false;
+  struct Col { float* dst; };
+  struct Pre { float o; };
+  __device__ __forceinline__ Col col(int n) const {
+    return {n < c1 ? out0 + n : (n < c2 ? out1 + (n - c1) : out2 + (n - c2))};
+  }
+  __device__ __forceinline__ Pre pre(int m, int, const Col& c) const {
+    return {accumulate ? c.dst[(int64_t)m * ldo] : 0.f};
+  }
+  __device__ __forceinline__ void apply(int m, int, float v, float, const Col& c,
+                                        const Pre& p) const {
+    c.dst[(int64_t)m * ldo] = v + p.o;
+  }
+};
+
 // Q/K/V projection: + bias, optional RoPE on interleaved pairs, scattered to a
 // head-major [heads, s, D] buffer. Everything that depends on the column only
 // (bias, destination head and offset, rotation role) is resolved once per

@@ -334,6 +334,25 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
   }
 }
 
+// dst[r, j] = src[r, off_k + (j - start_k)] for the three column segments
+// [0, c1), [c1, c2), [c2, n) of dst (start_k = 0, c1, c2): gathers a head
+// chunk's Q, K and V columns of the packed projection into one contiguous
+// block. One thread copies V elements (V = 1, or 16 bytes when the source
+// rows and every width and offset are 16-byte multiples).
+template <typename T, int V>
+__global__ __launch_bounds__(256) void gather_cols3_kernel(const T* __restrict__ src, int64_t lds,
+                                                           T* __restrict__ dst, int rows, int c1,
+                                                           int c2, int n, int64_t off0,
+                                                           int64_t off1, int64_t off2) {
+  struct Vec { T e[V]; };
+  const int vpr = n / V;  // vectors per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * vpr) return;
+  const int r = (int)(i / vpr), j = (int)(i - (int64_t)r * vpr) * V;
+  const int64_t sc = j < c1 ? off0 + j : (j < c2 ? off1 + (j - c1) : off2 + (j - c2));
+  *(Vec*)(dst + (int64_t)r * n + j) = *(const Vec*)(src + (int64_t)r * lds + sc);
+}
+
 __global__ __launch_bounds__(256) void fill_kernel(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
