@@ -203,7 +203,8 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
 template <typename T>
 struct BwdWs {
   T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t, *wc, *bc;
-  float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b;
+  float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b, *kbuf;
+  int64_t kbuf_floats;
   float2* rope;
 };
 
@@ -240,6 +241,10 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.part = c.take<float>(kColsumParts * maxn);
   w.npart_g = c.take<float>(kNormWaves * p.h);
   w.npart_b = c.take<float>(kNormWaves * p.h);
+  // Split-K partial sums of the sequence-long weight-gradient GEMMs (bf16
+  // path): s h / 4 floats, one byte per token and hidden unit.
+  w.kbuf_floats = p.dtype == BPT_BF16 ? p.s * p.h / 4 : 0;
+  w.kbuf = w.kbuf_floats ? c.take<float>(w.kbuf_floats) : nullptr;
   return w;
 }
 
@@ -286,7 +291,7 @@ int device_cus() {
 
 template <bool AK, bool BK, int BM, int BN, int BKK, int ST, int WM, int WN, int NW, class Epi>
 void launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
-                     int64_t M, int64_t N, int64_t K, const Epi& epi) {
+                     int64_t M, int64_t N, int64_t K, const Epi& epi, int ksplit = 1) {
   constexpr int kLds = ST * (BM + BN) * BKK * 2;
   auto kern = gemm_dma_kernel<AK, BK, BM, BN, BKK, ST, WM, WN, NW, Epi>;
   static std::once_flag attr_once;  // per instantiation
@@ -294,13 +299,19 @@ void launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, 
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   });
   const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)nt), dim3(64 * NW), kLds, st, A, lda, B, ldb, (int)M,
-                     (int)N, (int)K, epi);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nt * ksplit)), dim3(64 * NW), kLds, st, A, lda, B, ldb,
+                     (int)M, (int)N, (int)K, ksplit, epi);
 }
 
+// kbuf (kbuf_floats fp32 elements of workspace), when given, lets a weight
+// gradient with a long reduction (K >= 16384, the sequence) and too few output
+// tiles to fill the GPU run split-K: ksplit copies of the tile grid each sum
+// K / ksplit steps into kbuf, and a second kernel applies the epilogue to
+// their sum.
 template <typename T, bool AK, bool BK, class Epi>
 bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
-                int64_t N, int64_t K, const Epi& epi, const char* what) {
+                int64_t N, int64_t K, const Epi& epi, const char* what, float* kbuf = nullptr,
+                int64_t kbuf_floats = 0) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int BKK = sizeof(T) == 2 ? 64 : 32;
   // Layout invariants of the tile loaders (16-byte vectors along the
@@ -320,6 +331,22 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
       // traffic per flop of a 128 x 128 tile); smaller outputs use 128 x 128
       // tiles (waves of 32 x 64) to keep every CU busy.
       const int64_t nt256 = ((M + 255) / 256) * ((N + 255) / 256);
+      if constexpr (!AK && !BK && !Epi::kPair) {
+        if (kbuf && K >= 16384) {
+          int ks = 1;
+          while (nt256 * ks < 2 * device_cus() && ks < 64) ks *= 2;
+          while (ks > 1 && (ks * M * N > kbuf_floats || K % (ks * 64) != 0 || K / ks < 2048))
+            ks /= 2;
+          if (ks > 1) {
+            EpiPart ep{kbuf, N, M * N};
+            launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, ep,
+                                                                 ks);
+            hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((M * N + 255) / 256)),
+                               dim3(256), 0, st, kbuf, ks, (int)M, (int)N, epi);
+            return check_launch(what);
+          }
+        }
+      }
       if (nt256 >= device_cus()) {
         launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, epi);
       } else if (K >= 32768) {
@@ -713,7 +740,8 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     // dO = dh W_o^T.
     if (dwo) {
       EpiOut<T, float> e{dwo, p.h, nullptr, 1.f, 1};
-      BPT_TRY((gemm<T, false, false>(st, Ob, HD, w.dh_t, p.h, HD, p.h, p.s, e, "dWo")));
+      BPT_TRY((gemm<T, false, false>(st, Ob, HD, w.dh_t, p.h, HD, p.h, p.s, e, "dWo", w.kbuf,
+                                     w.kbuf_floats)));
     }
     {
       EpiOut<T, T> e{w.dO, HD, nullptr, 1.f, 0};
@@ -757,7 +785,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
         if (dwqkv) {
           EpiOut<T, float> e{dwqkv, p.qkv_cols, nullptr, 1.f, 1};
           BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, w.dqkv, p.chunk_cols, p.h, p.qkv_cols,
-                                         p.s, e, "dWqkv")));
+                                         p.s, e, "dWqkv", w.kbuf, w.kbuf_floats)));
         }
         BPT_TRY(colsum<T>(st, w.dqkv, p.chunk_cols, p.s, p.qkv_cols, w.part, dbqkv));
         EpiOut<T, float> e{w.dxn, p.h, nullptr, 1.f, 0};
@@ -774,7 +802,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
         EpiOut3<T> e{dwqkv + cc.off[0], dwqkv + cc.off[1], dwqkv + cc.off[2], p.qkv_cols,
                      (int)segc[1], (int)segc[2], 1};
         BPT_TRY((gemm<T, false, false>(st, w.xn, p.h, w.dqkv, p.chunk_cols, p.h, p.chunk_cols,
-                                       p.s, e, "dWqkv (chunk)")));
+                                       p.s, e, "dWqkv (chunk)", w.kbuf, w.kbuf_floats)));
       }
       for (int seg = 0; seg < 3; ++seg)
         BPT_TRY(colsum<T>(st, w.dqkv + segc[seg], p.chunk_cols, p.s, wid[seg], w.part,

@@ -117,6 +117,45 @@ struct EpiOut3 {
   }
 };
 
+// Split-K partial product: copy k of the split grid writes its raw fp32 sum
+// to out + k split_stride ([M, ldo] each); splitk_reduce_kernel then applies
+// the real epilogue to the sum of the copies.
+struct EpiPart {
+  float* out; int64_t ldo; int64_t split_stride;
+  static constexpr bool kPair = false;
+  struct Col {};
+  struct Pre {};
+  __device__ __forceinline__ Col col(int) const { return {}; }
+  __device__ __forceinline__ Pre pre(int, int, const Col&) const { return {}; }
+  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
+                                        const Pre&) const {
+    out[(int64_t)m * ldo + n] = v;
+  }
+};
+template <class Epi>
+__device__ __forceinline__ Epi epi_at_split(const Epi& e, int) { return e; }
+__device__ __forceinline__ EpiPart epi_at_split(const EpiPart& e, int k) {
+  EpiPart r = e;
+  r.out += k * e.split_stride;
+  return r;
+}
+
+// out = Epi(sum over k < nsplit of part[k, m, n]), one element per thread, the
+// copies summed in order (deterministic).
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int nsplit, int M, int N, Epi epi) {
+  const int64_t mn = (int64_t)M * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+  float v = 0.f;
+  for (int k = 0; k < nsplit; ++k) v += part[k * mn + i];
+  const typename Epi::Col c = epi.col(n);
+  const typename Epi::Pre p = epi.pre(m, n, c);
+  epi.apply(m, n, v, 0.f, c, p);
+}
+
 // Q/K/V projection: + bias, optional RoPE on interleaved pairs, scattered to a
 // head-major [heads, s, D] buffer. Everything that depends on the column only
 // (bias, destination head and offset, rotation role) is resolved once per

@@ -165,7 +165,7 @@ template <bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int STAGES, int WM, 
           class Epi>
 __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restrict__ A, int64_t lda,
                                                        const bf16* __restrict__ B, int64_t ldb,
-                                                       int M, int N, int K, Epi epi) {
+                                                       int M, int N, int K, int ksplit, Epi epi) {
   using OA = gdma::Operand<A_KMAJ, BM, BK>;
   using OB = gdma::Operand<B_KMAJ, BN, BK>;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
@@ -182,9 +182,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   // Same XCD-grouped tile order as gemm_kernel.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int nt = tiles_m * tiles_n;
+  // Split-K: the grid holds ksplit copies of the tile grid, copy k summing
+  // reduction steps [k K / ksplit, (k + 1) K / ksplit) (host: K % (ksplit BK) == 0).
+  const int split = blockIdx.x / nt;
   int tile;
   {
-    const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+    const int bid = blockIdx.x - split * nt, xcd = bid & 7, local = bid >> 3;
     const int q = nt >> 3, rem = nt & 7;
     tile = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
   }
@@ -203,13 +206,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
 
-  const int nk = K / BK;
+  const int nk = K / ksplit / BK, kbase = split * nk * BK;
   const typename OA::template Loader<NW> la(A, lda, m0, M, w, lane);
   const typename OB::template Loader<NW> lb(B, ldb, n0, N, w, lane);
   auto issue = [&](int kt) {
     char* st = smem + (kt % STAGES) * SBYTES;
-    la.issue(st, kt * BK, w);
-    lb.issue(st + ABYTES, kt * BK, w);
+    la.issue(st, kbase + kt * BK, w);
+    lb.issue(st + ABYTES, kbase + kt * BK, w);
   };
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -248,11 +251,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   }
 
   const int lr = lane & 31;
+  const Epi e = epi_at_split(epi, split);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      epilogue_block<false>(epi, acc[i][j], m0 + wm0 + 32 * i, n0 + wn0 + 32 * j + lr, g, M, N);
+      epilogue_block<false>(e, acc[i][j], m0 + wm0 + 32 * i, n0 + wn0 + 32 * j + lr, g, M, N);
 }
 
 }  // namespace bpt

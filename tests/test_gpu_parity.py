@@ -138,6 +138,25 @@ def test_batch_and_gradient_accumulation():
         assert err < 1e-6, (k, float(err))
 
 
+def test_split_k_weight_gradients_match_oracle():
+    """Weight gradients whose reduction runs over a long sequence (s >= 16384)
+    and whose output is too small to fill the GPU are summed split-K (partial
+    sums over sequence slices, then an ordered reduction). A dense cotangent
+    at s = 16384 with two head chunks exercises the split O-projection
+    gradient and the split, column-scattered chunk QKV gradient against the
+    oracle (tiny widths keep the float64 oracle to seconds)."""
+    sh = wl.WORKLOADS["gpt1b-s8k"].replace(
+        name="gpt1b-splitk", seq_len=16384, hidden=64, n_heads=2, n_kv_heads=2, head_dim=32,
+        ffn_dim=128, q_block=4096, kv_block=8192, head_chunk=1)
+    _say(f"[split-k] s={sh.seq_len} h={sh.hidden} H={sh.n_heads} U={sh.head_chunk}")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    gpu = run_gpu(inp)
+    ref = run_oracle(inp)
+    errs = compare(gpu, ref, sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
+    _say(f"  errs {errs}")
+    _check(errs, sh.dtype)
+
+
 # ----------------------------------------------------------------- full-size workloads
 FULL = ["gpt-tiny-fp32", "gpt1b-s8k", "gpt1b-s128k", "llama8b-s64k", "llama70b-s8k"]
 
