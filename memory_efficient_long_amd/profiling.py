@@ -2,6 +2,8 @@
 
     python -m memory_efficient_long_amd.profiling stats RUN_kernel_stats.csv \
         --out profiles/NAME.md --cmd "the command that produced it"
+    python -m memory_efficient_long_amd.profiling counters P1.csv P2.csv ... \
+        --out profiles/NAME.md --kernels REGEX --cmd "the command"
     python -m memory_efficient_long_amd.profiling traffic --kernel attn_bwd_dkdv_kernel \
         --workload gpt1b-s128k --fetch F.csv --write W.csv --calib-fetch CF.csv \
         --calib-write CW.csv --copy-bytes N --out profiles/KERNEL_WORKLOAD_traffic.json
@@ -97,6 +99,45 @@ def cmd_traffic(args) -> None:
         fh.write("\n")
 
 
+def cmd_counters(args) -> None:
+    """Per-kernel medians (over dispatches) of the counters in one or more
+    rocprofv3 --pmc runs, with a few ratios whose definitions are printed."""
+    per = {}  # kernel -> counter -> {dispatch: value}
+    for path in args.csv:
+        for r in csv.DictReader(open(path)):
+            name = short_name(r["Kernel_Name"])
+            if not re.search(args.kernels, name):
+                continue
+            d = per.setdefault(name, {}).setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    names = sorted({c for k in per.values() for c in k})
+    med = {k: {c: statistics.median(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+    lines = [f"# rocprofv3 counters: {args.title}", "", f"Command: `{args.cmd}`", "",
+             "Medians over the dispatches of each kernel (counter totals per dispatch).", "",
+             "| counter | " + " | ".join(f"`{k}`" for k in med) + " |",
+             "|---|" + "---|" * len(med)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(f"{med[k].get(c, float('nan')):.4g}" for k in med) + " |")
+    ratios = [
+        ("waiting share of wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+        ("LDS bank-conflict cycles per LDS-active cycle", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"),
+        ("VALU instructions per MFMA instruction", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+        ("LDS instructions per MFMA instruction", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+        ("L2 hit rate", "TCC_HIT_sum", ("TCC_HIT_sum", "TCC_MISS_sum")),
+    ]
+    lines += ["", "| ratio | " + " | ".join(f"`{k}`" for k in med) + " |",
+              "|---|" + "---|" * len(med)]
+    for label, num, den in ratios:
+        vals = []
+        for k in med:
+            m = med[k]
+            dv = sum(m.get(x, float("nan")) for x in den) if isinstance(den, tuple) else m.get(den, float("nan"))
+            vals.append(f"{m.get(num, float('nan')) / dv:.3f}" if dv else "nan")
+        lines.append(f"| {label} | " + " | ".join(vals) + " |")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -112,8 +153,14 @@ def main() -> None:
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--calib-kernel", default="copy")
     t.add_argument("--cmd", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--out", required=True)
+    c.add_argument("--kernels", default="attn_")
+    c.add_argument("--cmd", default="")
+    c.add_argument("--title", default="")
     args = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[args.cmd_name](args)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[args.cmd_name](args)
 
 
 if __name__ == "__main__":
