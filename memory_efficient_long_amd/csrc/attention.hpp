@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      const float2 mh = wave_halves(mx);
+      mx = fmaxf(mh.x, mh.y) * sl2;
       // Move the running max only when this tile exceeds it by > 8 (log2 units).
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
           sacc[sb][r] = p;
           rs += p;
         }
-      l_run += rs + shfl_xor(rs, 32);
+      const float2 rh = wave_halves(rs);
+      l_run += rh.x + rh.y;
       // P fragments: chunk cc covers keys 16cc + {8(e/4) + 4g + e%4}.
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {

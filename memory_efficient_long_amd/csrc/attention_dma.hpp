@@ -228,7 +228,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      const float2 mh = wave_halves(mx);
+      mx = fmaxf(mh.x, mh.y) * sl2;
       if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
         pf[cc] = pack_frag<bf16>(tmp);
         rs = row_sum_bf16x8(pf[cc], rs);
       }
-      l_run += rs + shfl_xor(rs, 32);
+      const float2 rh = wave_halves(rs);
+      l_run += rh.x + rh.y;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
