@@ -54,6 +54,11 @@ struct AttnBwdArgs {
   const float2* rope;                   // cos/sin [s, D/2] or null
   int s, nh, nkv, group, causal;
   float scale_log2, scale;              // log2(e)/sqrt(D), 1/sqrt(D)
+  // dK/dV split over the query heads of a KV head (bf16 head_dim 64/128):
+  // nparts > 1 runs nparts workgroups per key tile, each over group / nparts
+  // of the query heads, writing raw fp32 sums to part [nparts][2][nkv][s][D]
+  // (dK then dV) for dkdv_reduce_kernel.
+  float* part; int nparts;
 };
 
 // Map a workgroup id to (head, tile). Workgroups are dealt round-robin to the
@@ -240,8 +245,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      const float2 mh = wave_halves(mx);
-      mx = fmaxf(mh.x, mh.y) * sl2;
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
       // Move the running max only when this tile exceeds it by > 8 (log2 units).
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
@@ -262,8 +266,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
           sacc[sb][r] = p;
           rs += p;
         }
-      const float2 rh = wave_halves(rs);
-      l_run += rh.x + rh.y;
+      l_run += rs + shfl_xor(rs, 32);
       // P fragments: chunk cc covers keys 16cc + {8(e/4) + 4g + e%4}.
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {

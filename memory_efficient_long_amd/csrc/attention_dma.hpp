@@ -228,8 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      const float2 mh = wave_halves(mx);
-      mx = fmaxf(mh.x, mh.y) * sl2;
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
       if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
@@ -257,8 +256,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
         pf[cc] = pack_frag<bf16>(tmp);
         rs = row_sum_bf16x8(pf[cc], rs);
       }
-      const float2 rh = wave_halves(rs);
-      l_run += rh.x + rh.y;
+      l_run += rs + shfl_xor(rs, 32);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -289,7 +287,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
 }
 
 // ============================================================================ backward: dK, dV
-template <int D>
+// SPLIT: the query-head-split variant (a.nparts > 1, partial sums to a.part);
+// without it the part index is a compile-time zero and nothing of the split
+// remains in the code.
+template <int D, bool SPLIT = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<bf16> a) {
   using TL = DmaTile<D>;
   constexpr int BQ = 64, BKV = 128;
@@ -304,8 +305,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const int lr = lane & 31, g = lane >> 5;
   const int s = a.s;
   const int nkt = (s + BKV - 1) / BKV;
-  int hk, kt;
-  map_head_tile(blockIdx.x, a.nkv, nkt, false, hk, kt);
+  // Workgroup (KV head, part, key tile): part pp covers query heads
+  // [pp gp, (pp + 1) gp) of the KV head's group, gp = group / nparts.
+  const int np = SPLIT ? a.nparts : 1, gp = SPLIT ? a.group / np : a.group;
+  int vh, kt;
+  map_head_tile(blockIdx.x, a.nkv * np, nkt, false, vh, kt);
+  const int hk = SPLIT ? vh / np : vh, pp = SPLIT ? vh - hk * np : 0;
   const int kv0 = kt * BKV;
   const int kvrow = kv0 + 32 * w + lr;
   const bf16* Kp = a.k + (int64_t)hk * s * D;
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
   const int per_head = nqt - qt0;
-  const int nsteps = per_head * a.group;
+  const int nsteps = per_head * gp;
 
   // Row statistics of the next step: loaded raw (before the tile loads, so
   // waiting for them never waits for the tiles) and converted when stored.
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
   const typename TL::template Loader<BQ, 4> qld(D, lane), dold(a.lddo, lane);
   auto load_step = [&](int step, int buf) {
-    const int hq = hk * a.group + step / per_head;
+    const int hq = hk * a.group + pp * gp + step / per_head;
     const int q0 = (qt0 + step % per_head) * BQ;
     if (tid < BQ) {
       const int qr = q0 + tid;
@@ -472,6 +477,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     if (step + 1 < nsteps) q_step(step + 1, std::integral_constant<int, 1>());
   }
 
+  if constexpr (SPLIT) {  // raw partial sums; dkdv_reduce_kernel scales, rotates and converts
+    float* pk = a.part + ((int64_t)(2 * pp) * a.nkv + hk) * s * D;
+    float* pv = pk + (int64_t)a.nkv * s * D;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int d = 32 * i + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kv = kv0 + 32 * w + acc_row(r, g);
+        if (kv < s) {
+          pk[(int64_t)kv * D + d] = dkacc[i][r];
+          pv[(int64_t)kv * D + d] = dvacc[i][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
     const int d = 32 * i + lr;
@@ -490,6 +512,38 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       }
     }
   }
+}
+
+// dK, dV of the query-head-split pass: sums the nparts raw partials in
+// order, then applies 1/sqrt(D) and the inverse RoPE to dK as the unsplit
+// kernel does, and stores both in bf16. One thread per (row, KV head, pair of
+// columns).
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnBwdArgs<bf16> a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int s = a.s;
+  if (t >= (int64_t)s * a.nkv * (D / 2)) return;
+  const int dp = (int)(t % (D / 2));
+  const int64_t rh = t / (D / 2);
+  const int hk = (int)(rh % a.nkv), kv = (int)(rh / a.nkv);
+  const int64_t slab = (int64_t)a.nkv * s * D;
+  const int64_t off = ((int64_t)hk * s + kv) * D + 2 * dp;
+  float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+  for (int p = 0; p < a.nparts; ++p) {
+    const float2 pk = *(const float2*)(a.part + 2 * p * slab + off);
+    const float2 pv = *(const float2*)(a.part + (2 * p + 1) * slab + off);
+    k0 += pk.x; k1 += pk.y; v0 += pv.x; v1 += pv.y;
+  }
+  k0 *= a.scale; k1 *= a.scale;
+  if (a.rope) {
+    const float2 cs = a.rope[(int64_t)kv * (D / 2) + dp];
+    const float r0 = k0 * cs.x + k1 * cs.y, r1 = k1 * cs.x - k0 * cs.y;
+    k0 = r0; k1 = r1;
+  }
+  bf16* dk = a.dk + (int64_t)kv * a.lddkv + (int64_t)hk * D + 2 * dp;
+  bf16* dv = a.dv + (int64_t)kv * a.lddkv + (int64_t)hk * D + 2 * dp;
+  dk[0] = (bf16)k0; dk[1] = (bf16)k1;
+  dv[0] = (bf16)v0; dv[1] = (bf16)v1;
 }
 
 // ============================================================================ backward: dQ

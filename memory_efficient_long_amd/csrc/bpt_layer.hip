@@ -101,6 +101,7 @@ constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
 // taller, a quarter of the launches, and one read-modify-write of the fp32
 // dW_1 / dW_2 per group. The FFN scratch stays O(c_q f): no s x f term.
 constexpr int64_t kGradGroupBlocks = 4;
+constexpr int kDkvMaxParts = 4;  // query-head split of the dK/dV pass (see attn_bwd)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -161,6 +162,16 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
   return BPT_OK;
 }
 
+// Largest query-head split of the dK/dV pass that the workspace provides for:
+// a power of two dividing G, at most kDkvMaxParts, for bf16 with head_dim 64
+// or 128 and fewer than 8 KV heads per chunk (more give enough workgroups).
+int dkv_parts_max(const Plan& p) {
+  if (p.dtype != BPT_BF16 || (p.D != 64 && p.D != 128) || p.nkvc >= 8) return 1;
+  int m = 1;
+  while (m < kDkvMaxParts && p.G % (2 * m) == 0) m *= 2;
+  return m;
+}
+
 // Workspace carve-up: a running offset over 256-byte aligned regions.
 struct Carver {
   char* base; size_t off = 0;
@@ -203,7 +214,7 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
 template <typename T>
 struct BwdWs {
   T *xn, *q, *k, *v, *dO, *dqkv, *z, *a, *u, *up, *da, *dup, *dh_t, *wc, *bc;
-  float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b, *kbuf;
+  float *dvec, *dh, *dxn, *h1, *dz, *part, *npart_g, *npart_b, *kbuf, *dkv_part;
   int64_t kbuf_floats;
   float2* rope;
 };
@@ -245,6 +256,10 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   // path): s h / 4 floats, one byte per token and hidden unit.
   w.kbuf_floats = p.dtype == BPT_BF16 ? p.s * p.h / 4 : 0;
   w.kbuf = w.kbuf_floats ? c.take<float>(w.kbuf_floats) : nullptr;
+  // Partial dK/dV sums of the query-head split (bf16, GQA with fewer than 8
+  // KV heads per chunk): parts x 2 x (KV heads of a chunk) x s x d fp32.
+  const int parts = dkv_parts_max(p);
+  w.dkv_part = parts > 1 ? c.take<float>((int64_t)parts * 2 * p.nkvc * p.s * p.D) : nullptr;
   return w;
 }
 
@@ -490,8 +505,10 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
 template <typename T>
 bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v,
                     const T* dout, const float* lse, const float* dvec, T* dq, T* dk, T* dv,
-                    const float2* rope) {
+                    const float2* rope, float* dkv_part) {
   AttnBwdArgs<T> a;
+  a.part = nullptr;
+  a.nparts = 1;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.lddo = p.H * p.D; a.lse = lse; a.dvec = dvec;
   a.dq = dq; a.lddq = p.chunk_cols; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
   a.s = (int)p.s; a.nh = (int)p.U; a.nkv = (int)p.nkvc; a.group = (int)p.G; a.causal = p.causal;
@@ -505,8 +522,27 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DKDV, st);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), gkv, blk, 0, st, a); done = true; }
-      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64>), gkv, blk, 0, st, a); done = true; }
+      // Few KV heads per chunk leave too few key-tile workgroups to balance
+      // the causal work (the first key tile of a head carries the most):
+      // split each KV head's query heads over up to kDkvMaxParts workgroups.
+      const int64_t wgs = p.nkvc * ((p.s + 127) / 128);
+      if (dkv_part)
+        while (a.nparts < dkv_parts_max(p) && wgs * a.nparts < 8 * device_cus()) a.nparts *= 2;
+      if (a.nparts > 1) a.part = dkv_part;
+      const dim3 gsplit((unsigned)(wgs * a.nparts));
+      if (a.nparts > 1) {
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, true>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, true>), gsplit, blk, 0, st, a);
+      } else {
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64>), gsplit, blk, 0, st, a);
+      }
+      done = p.D == 128 || p.D == 64;
+      if (a.nparts > 1) {
+        const dim3 gr((unsigned)((p.s * p.nkvc * (p.D / 2) + 255) / 256));
+        if (p.D == 128) hipLaunchKernelGGL((dkdv_reduce_kernel<128>), gr, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((dkdv_reduce_kernel<64>), gr, blk, 0, st, a);
+      }
     }
     if (!done) {
       if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
@@ -775,7 +811,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       T* dK = w.dqkv + p.U * p.D;
       T* dV = w.dqkv + (p.U + p.nkvc) * p.D;
       BPT_TRY(attn_bwd<T>(st, p, w.q, w.k, w.v, w.dO + hq0 * p.D, Lb + hq0 * p.s,
-                          w.dvec + hq0 * p.s, w.dqkv, dK, dV, w.rope));
+                          w.dvec + hq0 * p.s, w.dqkv, dK, dV, w.rope, w.dkv_part));
       const int64_t segc[3] = {0, p.U * p.D, (p.U + p.nkvc) * p.D};
       const int64_t wcol[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
       const int64_t wid[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};

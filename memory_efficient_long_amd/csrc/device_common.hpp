@@ -128,16 +128,6 @@ __device__ __forceinline__ void transpose_4xvec(const u32x4 in[4], u32x4 out[4])
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
-// The values of x in lanes l and l ^ 32 (the two halves of the wave), in the
-// same order on both lanes (lower half first): one v_permlane32_swap, a VALU
-// operation, where a 32-lane xor shuffle would go through the LDS crossbar.
-__device__ __forceinline__ float2 wave_halves(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return make_float2(__builtin_bit_cast(float, (unsigned)r[0]),
-                     __builtin_bit_cast(float, (unsigned)r[1]));
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // acc + sum of the eight bf16 values of v: four v_dot2c_f32_bf16 with
