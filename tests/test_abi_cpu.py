@@ -175,6 +175,24 @@ def test_memory_is_affine_in_s_without_s_times_ffn(backward):
     assert sizes[3][1] == sh.seq_len * sh.n_heads * sh.head_dim * 2 + sh.n_heads * sh.seq_len * 4
 
 
+@pytest.mark.parametrize("head_chunk", [4, 8, 32])
+def test_gqa_workspace_is_affine_in_s(head_chunk):
+    """GQA with few KV heads per chunk adds the dK/dV split partials and the
+    gathered chunk weights; the backward workspace stays affine in s."""
+    base = wl.WORKLOADS["llama8b-s64k"].replace(head_chunk=head_chunk)
+
+    def ws(s):
+        d = bpt.LayerConfig.from_shape(base.replace(seq_len=s)).desc()
+        return bpt.bpt_layer_workspace_size(d, True)
+
+    sizes = [ws(s) for s in (16384, 32768, 65536, 131072)]
+    d1 = sizes[1] - sizes[0]
+    d2 = (sizes[2] - sizes[1]) / 2
+    d3 = (sizes[3] - sizes[2]) / 4
+    assert abs(d1 - d2) <= 8192 and abs(d2 - d3) <= 8192
+    assert d1 > 0
+
+
 def test_weight_set_matches_printed_parameter_counts(repo_root):
     """12h^2 + 13h per GPT layer ("Training memory", §3 parameters and §4/§5
     printed values)."""
