@@ -221,11 +221,14 @@ def main() -> int:
     # bf16 with head_dim 64 / 128 runs the direct-to-LDS attention kernels.
     dma = sh.dtype == "bf16" and sh.head_dim in (64, 128)
     kernel_name = dom + ("_dma_kernel" if dma else "_kernel")
+    traffic = (load_traffic(kernel_name, sh.name)
+               if sh.head_chunk == wl.WORKLOADS[args.workload].head_chunk else None)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 # counters are taken at the workload's own head chunk
-                "traffic": (load_traffic(kernel_name, sh.name)
-                            if sh.head_chunk == wl.WORKLOADS[args.workload].head_chunk else None),
+                "traffic": traffic,
+                "traffic_gb_per_s": (round(traffic / (avg_ms * 1e-3) / 1e9, 1)
+                                     if traffic and avg_ms > 0 else None),
                 "kernel": kernel_name,
                 "avg_launch_ms": round(avg_ms, 3), "launches_per_step": dom_n / args.steps,
                 "algorithmic_flops_per_launch": per_launch_flops,
@@ -264,7 +267,10 @@ def main() -> int:
                    "saved_sbh": round(saved_bytes / (tokens * sh.hidden), 3),
                    "peak_bytes_per_token": (saved_bytes + max(ws_f_bytes, ws_b_bytes)) / tokens,
                    "peak_sbh": round((saved_bytes + max(ws_f_bytes, ws_b_bytes)) / (tokens * sh.hidden), 3),
-                   "pages_bpt_sbh": 2, "pages_flashattention_ffn_sbh": 8},
+                   "pages_bpt_sbh": 2, "pages_flashattention_ffn_sbh": 8,
+                   # cross-check: everything this process allocated on the GPU
+                   # (inputs, weights, gradients, saved state, workspaces)
+                   "torch_max_allocated_bytes": int(torch.cuda.max_memory_allocated(dev))},
         "roofline": roofline,
         "cpu_baseline": None,
     }
