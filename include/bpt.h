@@ -117,8 +117,8 @@ bpt_status bpt_layer_validate(const bpt_layer_desc* desc);
 size_t bpt_layer_saved_size(const bpt_layer_desc* desc);
 
 /* Workspace bytes for the forward (backward = 0) or the backward (backward = 1). Affine in s
- * with no s * ffn_dim term (the FFN scratch covers at most four query blocks: 4 q_block x
- * ffn_dim). Returns 0 for an invalid descriptor. */
+ * with no s * ffn_dim term (the FFN scratch covers one group of query blocks, about 8192 rows
+ * or one block if larger, times ffn_dim). Returns 0 for an invalid descriptor. */
 size_t bpt_layer_workspace_size(const bpt_layer_desc* desc, int32_t backward);
 
 /* Forward. x, y: [b, s, h]. saved: bpt_layer_saved_size bytes, written here and read by the

@@ -100,7 +100,11 @@ constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
 // on groups of up to this many consecutive query blocks: GEMMs four times
 // taller, a quarter of the launches, and one read-modify-write of the fp32
 // dW_1 / dW_2 per group. The FFN scratch stays O(c_q f): no s x f term.
-constexpr int64_t kGradGroupBlocks = 4;
+// The FFN (forward and backward) runs over groups of consecutive query blocks
+// of about this many rows: the weight gradients reduce over a group's rows,
+// and at 8192 rows their GEMMs run near the speed of the sequence-long ones
+// while the scratch stays independent of s.
+constexpr int64_t kFfnGroupRows = 8192;
 constexpr int kDkvMaxParts = 4;  // query-head split of the dK/dV pass (see attn_bwd)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -156,7 +160,7 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
   p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
   p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
   p.chunk_cols = (p.U + 2 * p.nkvc) * p.D;
-  p.gq = std::min<int64_t>(p.s / p.cq, kGradGroupBlocks);
+  p.gq = std::min<int64_t>(p.s / p.cq, std::max<int64_t>(1, kFfnGroupRows / p.cq));
   p.rope_base = d->rope_base; p.eps = d->norm_eps;
   p.esz = d->dtype == BPT_BF16 ? 2 : 4;
   return BPT_OK;

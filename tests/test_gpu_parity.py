@@ -138,16 +138,18 @@ def test_batch_and_gradient_accumulation():
         assert err < 1e-6, (k, float(err))
 
 
-def test_split_k_weight_gradients_match_oracle():
+def test_split_k_weight_gradients_and_ffn_groups_match_oracle():
     """Weight gradients whose reduction runs over a long sequence (s >= 16384)
     and whose output is too small to fill the GPU are summed split-K (partial
-    sums over sequence slices, then an ordered reduction). A dense cotangent
-    at s = 16384 with two head chunks exercises the split O-projection
-    gradient and the split, column-scattered chunk QKV gradient against the
-    oracle (tiny widths keep the float64 oracle to seconds)."""
+    sums over sequence slices, then an ordered reduction); the FFN runs over
+    groups of query blocks of about 8192 rows. A dense cotangent at s = 20480
+    with two head chunks and five query blocks of 4096 rows (FFN groups of
+    2, 2 and 1 blocks) exercises the split O-projection gradient, the split,
+    column-scattered chunk QKV gradient and a partial last FFN group against
+    the oracle (tiny widths keep the float64 oracle to seconds)."""
     sh = wl.WORKLOADS["gpt1b-s8k"].replace(
-        name="gpt1b-splitk", seq_len=16384, hidden=64, n_heads=2, n_kv_heads=2, head_dim=32,
-        ffn_dim=128, q_block=4096, kv_block=8192, head_chunk=1)
+        name="gpt1b-splitk", seq_len=20480, hidden=64, n_heads=2, n_kv_heads=2, head_dim=32,
+        ffn_dim=128, q_block=4096, kv_block=4096, head_chunk=1)
     _say(f"[split-k] s={sh.seq_len} h={sh.hidden} H={sh.n_heads} U={sh.head_chunk}")
     inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
     gpu = run_gpu(inp)

@@ -111,8 +111,8 @@ SMALL: Dict[str, LayerShape] = {
     # in fp32 only: in bf16 the pre-activation is recomputed from bf16-stored
     # values, and where it lies within rounding of 0 the ReLU derivative flips,
     # an O(1) difference per such element that no tolerance on rounding covers.)
-    # Five query blocks: the backward's weight gradients run as a group of
-    # four blocks and a group of one.
+    # Five query blocks (one FFN group here; the parity test at s = 20480
+    # covers FFN groups of 2, 2 and 1 blocks).
     "gpt1b-small-5blocks": WORKLOADS["gpt1b-s8k"].replace(
         name="gpt1b-small-5blocks", seq_len=640, hidden=256, n_heads=2, n_kv_heads=2,
         ffn_dim=512, q_block=128, kv_block=320, head_chunk=2),
