@@ -223,14 +223,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
           for (int r = 0; r < 16; ++r)
             sacc[sb][r] = (32 * sb + acc_row(r, g) > lim) ? -INFINITY : sacc[sb][r];
       }
+      // A query's 64 keys of the tile are split between lanes l and l + 32;
+      // each half tests its own maximum (the running max is common to both),
+      // and the two are combined (an LDS shuffle) only on the rare tiles
+      // where the running max must move.
       float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      mx *= sl2;
       if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = fmaxf(m_run, fmaxf(mx, shfl_xor(mx, 32)));
         const float alpha = fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
