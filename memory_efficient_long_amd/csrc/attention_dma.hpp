@@ -251,16 +251,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       // over the same bf16 values, two per dot-product instruction, so the
       // normaliser matches what the MFMAs accumulate.
       bf16x8 pf[4];
-      float rs = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         float tmp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) tmp[e] = sacc[cc >> 1][8 * (cc & 1) + e];
         pf[cc] = pack_frag<bf16>(tmp);
-        rs = row_sum_bf16x8(pf[cc], rs);
       }
-      l_run += rs + shfl_xor(rs, 32);
+      // this half's 32 keys; the halves share the running max and are added
+      // once, after the last tile
+      l_run += row_sum_bf16x32(pf);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -275,6 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
     if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
+  l_run += shfl_xor(l_run, 32);  // both halves' sums
   if (wave_active && qrow < s) {
     const float inv_l = 1.f / l_run;
     bf16* orow = a.o + (int64_t)qrow * a.ldo + (int64_t)hq * D;

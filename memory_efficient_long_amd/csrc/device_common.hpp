@@ -130,13 +130,37 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// acc + sum of the eight bf16 values of v: four v_dot2c_f32_bf16 with
-// (1.0, 1.0). Written as inline asm: the builtin's vector operands were
-// observed to be mis-selected (one dword used for all four products).
-__device__ __forceinline__ float row_sum_bf16x8(const bf16x8& v, float acc) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(u[k]));
+// Sum of the 32 bf16 values of v[0..3]: sixteen v_dot2c_f32_bf16 with
+// (1.0, 1.0) accumulating into one register. Written as inline asm (the
+// builtin's vector operands were observed to be mis-selected, one dword used
+// for all four products), in one block that ends with three wait states: a
+// different VALU instruction may read a dot-product result only three wait
+// states after it is written, and the compiler's hazard tracking does not
+// see into inline assembly.
+__device__ __forceinline__ float row_sum_bf16x32(const bf16x8 (&v)[4]) {
+  const u32x4 a = __builtin_bit_cast(u32x4, v[0]), b = __builtin_bit_cast(u32x4, v[1]);
+  const u32x4 c = __builtin_bit_cast(u32x4, v[2]), d = __builtin_bit_cast(u32x4, v[3]);
+  float acc = 0.f;
+  asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %2\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %3\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %4\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %5\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %6\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %7\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %8\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %9\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %10\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %11\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %12\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %13\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %14\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %15\n\t"
+      "v_dot2c_f32_bf16 %0, 0x3f803f80, %16\n\t"
+      "s_nop 2"
+      : "+v"(acc)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]),
+        "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]));
   return acc;
 }
 
