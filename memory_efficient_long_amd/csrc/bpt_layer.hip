@@ -313,10 +313,19 @@ void launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, 
                      int64_t M, int64_t N, int64_t K, const Epi& epi, int ksplit = 1) {
   constexpr int kLds = ST * (BM + BN) * BKK * 2;
   auto kern = gemm_dma_kernel<AK, BK, BM, BN, BKK, ST, WM, WN, NW, Epi>;
-  static std::once_flag attr_once;  // per instantiation
-  std::call_once(attr_once, [&] {
+  // The dynamic-LDS limit is raised once per instantiation and device (a bit
+  // per device in `raised`; setting it twice from racing threads is harmless).
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    const uint64_t bit = 1ull << dev;
+    if (!(raised.load(std::memory_order_acquire) & bit)) {
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      raised.fetch_or(bit, std::memory_order_release);
+    }
+  } else {
     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-  });
+  }
   const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nt * ksplit)), dim3(64 * NW), kLds, st, A, lda, B, ldb,
                      (int)M, (int)N, (int)K, ksplit, epi);
