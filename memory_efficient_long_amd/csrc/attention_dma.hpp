@@ -291,6 +291,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   }
 }
 
+// Value of lane R of this lane's 16-lane row (DPP row_newbcast).
+template <int R>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + R, 0xF, 0xF, false));
+}
+template <int... R>
+__device__ __forceinline__ void seed_rows(f32x16& s, f32x16& d, float xs, float xd,
+                                          std::integer_sequence<int, R...>) {
+  ((s[R] = row_bcast<R>(xs), d[R] = row_bcast<R>(xd)), ...);
+}
+
 // ============================================================================ backward: dK, dV
 // SPLIT: the query-head-split variant (a.nparts > 1, partial sums to a.part);
 // without it the part index is a compile-time zero and nothing of the split
@@ -397,12 +409,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       // Seeding the accumulators with -lse (score units) and -D_i puts the row
       // statistics where the products land, with no extra registers.
       f32x16 sacc, dpacc;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 l4 = ld<f32x4>(&lse_s[buf][32 * qb + 8 * k + 4 * g]);
-        const f32x4 d4 = ld<f32x4>(&dd_s[buf][32 * qb + 8 * k + 4 * g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { sacc[4 * k + j] = l4[j]; dpacc[4 * k + j] = d4[j]; }
+      {
+        // Element r of a lane's accumulators is query 32 qb + 8 (r / 4) +
+        // 4 g + r % 4: lane n of each 16-lane row reads the statistics of
+        // query 32 qb + 8 (n / 4) + 4 g + n % 4 (one LDS read each), and
+        // element r is broadcast from lane r of the row (g is constant
+        // within a row) -- two 4-byte reads per query block instead of
+        // eight 16-byte ones.
+        const int n16 = lane & 15;
+        const int qi = 32 * qb + (n16 >> 2) * 8 + 4 * g + (n16 & 3);
+        const float xl = lse_s[buf][qi], xd = dd_s[buf][qi];
+        seed_rows(sacc, dpacc, xl, xd, std::make_integer_sequence<int, 16>());
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -416,12 +433,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         dpacc = mma(TL::frag_at(dosa + buf * TB, rf, qb, c), vf[c], dpacc);
       }
       // Order hint (sched_group_barrier; 0x100 = LDS reads, 0x008 = MFMA): the
-      // eight statistics reads and the first PF fragment reads, then each MFMA
+      // two statistics reads and the first PF fragment reads, then each MFMA
       // followed by the next fragment read, so a read is issued PF MFMAs before
       // its use instead of right before it.
       {
         constexpr int PF = 2;
-        __builtin_amdgcn_sched_group_barrier(0x100, 8 + PF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + PF, 0);
 #pragma unroll
         for (int m = 0; m < 2 * NC - PF; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
