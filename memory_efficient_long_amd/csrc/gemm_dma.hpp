@@ -191,7 +191,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
     const int q = nt >> 3, rem = nt & 7;
     tile = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + local;
   }
-  constexpr int GROUP = 8;
+  // Tiles in column-major order within bands of GROUP tile rows, so the
+  // workgroups resident on an XCD share A rows and B columns in its L2
+  // (four rows per band measured ~2 % faster than eight on these shapes).
+  constexpr int GROUP = 4;
   const int group = tile / (GROUP * tiles_n);
   const int first_m = group * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
