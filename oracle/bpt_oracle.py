@@ -149,6 +149,22 @@ def attention_probs(q_h, k_h, rows, causal):
     return e / e.sum(axis=1, keepdims=True)
 
 
+# Query rows per explicit score matrix. The softmax is defined row by row, so
+# evaluating the rows in groups changes nothing but the size of the temporary
+# (a group x keys matrix instead of rows x keys); with the causal mask a group
+# needs only the keys up to its last row, since every later key has weight
+# exactly zero (exp(-inf) = 0) for all of its rows.
+ROW_GROUP = 2048
+
+
+def _row_groups(rows, n, causal):
+    """(slice of ``rows``, number of keys) for each group of query rows."""
+    for a in range(0, len(rows), ROW_GROUP):
+        sl = slice(a, min(a + ROW_GROUP, len(rows)))
+        nk = int(rows[sl.stop - 1]) + 1 if causal else n
+        yield sl, nk
+
+
 # --------------------------------------------------------------------------- FFN
 def _gelu(a):
     return 0.5 * a * (1.0 + erf(a / np.sqrt(2.0)))
@@ -205,8 +221,9 @@ def _sequence(x, w, sp: Spec, rows, dy):
     attn = np.empty((r, H, d))
     for hq in range(H):
         kv = hq // G
-        p = attention_probs(q[:, hq], k[:, kv], rows, sp.causal)
-        attn[:, hq] = p @ v[:, kv]
+        for sl, nk in _row_groups(rows, n, sp.causal):
+            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal)
+            attn[sl, hq] = p @ v[:nk, kv]
     attn2 = attn.reshape(r, H * d)
 
     h1 = x[rows] + attn2 @ w_o + (b_o if b_o is not None else 0.0)
@@ -259,12 +276,13 @@ def _sequence(x, w, sp: Spec, rows, dy):
     dv = np.zeros((n, Hkv, d))
     for hq in range(H):
         kv = hq // G
-        p = attention_probs(q[:, hq], k[:, kv], rows, sp.causal)
-        dp = dattn[:, hq] @ v[:, kv].T
-        dv[:, kv] += p.T @ dattn[:, hq]
-        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-        dq[:, hq] = ds @ k[:, kv] / np.sqrt(d)
-        dk[:, kv] += ds.T @ q[:, hq] / np.sqrt(d)
+        for sl, nk in _row_groups(rows, n, sp.causal):
+            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal)
+            dp = dattn[sl, hq] @ v[:nk, kv].T
+            dv[:nk, kv] += p.T @ dattn[sl, hq]
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[sl, hq] = ds @ k[:nk, kv] / np.sqrt(d)
+            dk[:nk, kv] += ds.T @ q[sl, hq] / np.sqrt(d)
     if sp.rope_base is not None:
         dq = rope_rotate(dq, rows, sp.rope_base, sign=-1.0)
         dk = rope_rotate(dk, np.arange(n), sp.rope_base, sign=-1.0)

@@ -99,8 +99,12 @@ def _rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
+@pytest.mark.parametrize("row_group", [orc.ROW_GROUP, 5])
 @pytest.mark.parametrize("variant", list(VARIANTS))
-def test_layer_matches_torch_library_and_autograd(variant):
+def test_layer_matches_torch_library_and_autograd(variant, row_group, monkeypatch):
+    # row_group 5 splits the 24 query rows into groups of 5 (the last one
+    # ragged), each against only the keys up to its last row when causal.
+    monkeypatch.setattr(orc, "ROW_GROUP", row_group)
     kw = dict(VARIANTS[variant])
     sh = _shape(s=24, d=8, f=48, **{**kw, "h": kw.get("h", 16)})
     w = _weights(sh)
@@ -334,10 +338,12 @@ def test_norm_statistics():
     assert np.max(np.abs(dx.sum(axis=1))) < 1e-12
 
 
+@pytest.mark.parametrize("row_group", [orc.ROW_GROUP, 3])
 @pytest.mark.parametrize("variant", ["gpt-gelu", "llama-gqa-rope-swiglu", "noncausal-gelu"])
-def test_row_subset_matches_dense(variant):
+def test_row_subset_matches_dense(variant, row_group, monkeypatch):
     """The rows/sparse-cotangent mode (used at full sizes) equals the dense layer
     with dy zero outside the chosen rows."""
+    monkeypatch.setattr(orc, "ROW_GROUP", row_group)
     kw = dict(VARIANTS[variant])
     sh = _shape(s=40, d=8, f=48, **{**kw, "h": kw.get("h", 16)})
     w = _weights(sh)
