@@ -5,17 +5,19 @@
  * "Blockwise Parallel Transformer for Long Context Large Models" (§3.2 the
  * two nested loops, §3.4 the online softmax, Algorithm 1 and the memory
  * analysis): for every query block, key/value blocks stream through an online
- * softmax (running max and sum, no s x s score matrix), and the block's
- * attention output goes straight through the output projection, the residual,
- * the second norm and the position-wise FFN, so neither the s x s scores nor
- * the s x ffn_dim FFN intermediate is ever materialised. The backward
- * recomputes what it needs per query block ("recomputation is also done
- * blockwise", same page, memory analysis) and rebuilds attention scores from
- * the saved output and per-row log-sum-exp ("Training memory: model states,
- * activations and checkpointing", §3, what changes the count: FlashAttention
- * keeps O and one fp32 log-sum-exp per row and head). An optional head-chunk
- * loop runs a subset of heads at a time ("Untied Ulysses: Memory-Efficient
- * Context Parallelism via Headwise Chunking", §3.2 and §3.4).
+ * softmax (running max and sum, no s x s score matrix); the attention outputs
+ * of all query blocks are written to the saved buffer, the output projection
+ * and residual run over the whole sequence (a position-wise product), and
+ * Norm2 and the position-wise FFN run over groups of whole query blocks (at
+ * most 8192 rows and at most half the sequence; one block if larger), so
+ * neither the s x s scores nor an s x ffn_dim FFN intermediate is ever
+ * materialised. The backward recomputes what it needs ("recomputation is
+ * also done blockwise", same page, memory analysis) and rebuilds attention
+ * scores from the saved output and per-row log-sum-exp ("Training memory:
+ * model states, activations and checkpointing", §3, what changes the count:
+ * FlashAttention keeps O and one fp32 log-sum-exp per row and head). An
+ * optional head-chunk loop runs a subset of heads at a time ("Untied Ulysses:
+ * Memory-Efficient Context Parallelism via Headwise Chunking", §3.2 and §3.4).
  *
  *   h1 = x + Attn(Norm1(x)) W_o + b_o,   y = h1 + FFN(Norm2(h1))
  *
@@ -81,7 +83,8 @@ typedef struct {
   int64_t n_kv_heads;  /* KV heads; divides H; query head q uses KV head q / (H / n_kv_heads) */
   int64_t head_dim;    /* d in {32, 64, 128} */
   int64_t ffn_dim;     /* f; multiple of 64 */
-  int64_t q_block;     /* c_q: rows per BPT query block (the FFN block); divides s, multiple of 8 */
+  int64_t q_block;     /* c_q: rows per BPT query block; divides s, multiple of 8. Norm2 and the
+                          FFN run on groups of whole query blocks (see the file comment). */
   int64_t kv_block;    /* c_kv: key/value block of the online softmax; divides s. Results do not
                           depend on it; the kernel streams K/V through LDS in 64-row tiles. */
   int64_t head_chunk;  /* U: query heads per stage; divides H and is a multiple of H / n_kv_heads */
@@ -108,34 +111,54 @@ typedef struct {
   int32_t reserved;
 } bpt_layer_grads;
 
-/* Host-only check of a descriptor (no device work). */
+/* Host-only check of a descriptor (no device work): the shape rules above, the block sizes
+ * dividing s ("Blockwise Parallel Transformer...", §3.4, the sequence split into blocks),
+ * head_chunk holding whole GQA groups ("Untied Ulysses...", §3.4, each stage projects the KV
+ * heads its query heads use) and the built combinations (head_dim 32/64/128; fp32 only up to
+ * head_dim 64; hidden up to 16384). Returns BPT_OK, BPT_EINVAL or BPT_EUNSUPPORTED and
+ * leaves a message in bpt_last_error(). */
 bpt_status bpt_layer_validate(const bpt_layer_desc* desc);
 
 /* Bytes of the forward->backward state: the attention output O [b, s, H d] in the storage
- * dtype plus one fp32 base-2 log-sum-exp per (batch, head, row). Linear in s. Returns 0 for an
- * invalid descriptor. */
+ * dtype plus one fp32 base-2 log-sum-exp per (batch, head, row) ("Training memory...", §3:
+ * the FlashAttention saved set, O plus one fp32 statistic per row and head; "Blockwise
+ * Parallel Transformer...", §3.4 memory analysis: about 2bsh per layer). Linear in s.
+ * Returns 0 for an invalid descriptor. */
 size_t bpt_layer_saved_size(const bpt_layer_desc* desc);
 
 /* Workspace bytes for the forward (backward = 0) or the backward (backward = 1). Affine in s
- * with no s * ffn_dim term (the FFN scratch covers one group of query blocks, about 8192 rows
- * or one block if larger, times ffn_dim). Returns 0 for an invalid descriptor. */
+ * with no s * ffn_dim term ("Blockwise Parallel Transformer...", §3.2: the FFN intermediate
+ * exists for one query block at a time; here for one group of whole query blocks of at most
+ * min(8192, s / 2) rows, or one block if larger). Returns 0 for an invalid descriptor. */
 size_t bpt_layer_workspace_size(const bpt_layer_desc* desc, int32_t backward);
 
-/* Forward. x, y: [b, s, h]. saved: bpt_layer_saved_size bytes, written here and read by the
- * backward. ws: workspace (256-byte aligned), contents undefined on return. stream: a
- * hipStream_t (NULL = the default stream). */
+/* Forward of the layer ("Blockwise Parallel Transformer...", §3.2 and Algorithm 1: blockwise
+ * attention with the online softmax of §3.4, then the FFN per query block, with residuals;
+ * pre-norm placement as in "Training memory...", §5 code). x, y: [b, s, h] in the storage
+ * dtype, device memory, 16-byte aligned. saved: bpt_layer_saved_size bytes (16-byte aligned),
+ * written here and read by the backward. ws: workspace of at least
+ * bpt_layer_workspace_size(desc, 0) bytes, 256-byte aligned; contents undefined on return.
+ * stream: a hipStream_t (NULL = the default stream). Inputs are not modified. Returns
+ * BPT_EINVAL / BPT_EWORKSPACE / BPT_EUNSUPPORTED before any launch, BPT_EHIP if a launch
+ * fails (then y and saved are undefined). */
 bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x,
                              const bpt_layer_weights* w, void* y, void* saved, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* Recompute-based backward. x: the forward's input; saved: the forward's saved buffer;
- * dy: cotangent of y [b, s, h]; dx: [b, s, h] (storage dtype) written; grads: fp32 parameter
- * gradients (summed over the batch). */
+/* Recompute-based backward ("Blockwise Parallel Transformer...", §3.4 memory analysis: the
+ * backward recomputes blockwise; "Training memory...", §2 per-operation gradient rules and §3
+ * FlashAttention backward from O and the log-sum-exp). x: the forward's input; saved: the
+ * forward's saved buffer (unchanged); dy: cotangent of y [b, s, h]; dx: [b, s, h] (storage
+ * dtype) written; grads: fp32 parameter gradients (summed over the batch), 4-byte aligned,
+ * overwritten or accumulated per grads->accumulate. ws: at least
+ * bpt_layer_workspace_size(desc, 1) bytes, 256-byte aligned. Same error behaviour as the
+ * forward; on BPT_EHIP dx and the gradients are undefined. */
 bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x,
                               const bpt_layer_weights* w, const void* saved, const void* dy,
                               void* dx, const bpt_layer_grads* grads, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Static description of a status code (never NULL). */
 const char* bpt_status_string(bpt_status status);
 
 /* ---- Kernel timing (instrumentation for benchmarks and profiling) ----

@@ -20,7 +20,7 @@ __all__ = [
     "bpt_layer_forward", "bpt_layer_backward", "bpt_status_string", "bpt_last_error",
     "forward", "backward", "WEIGHT_NAMES", "GRAD_NAMES", "bpt_timing_enable", "bpt_timing_read",
     "bpt_mfma_peak_probe",
-    "KERNEL_CLASSES",
+    "KERNEL_CLASSES", "check_forward_args", "check_backward_args", "weight_shapes_of",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -213,6 +213,106 @@ def _weights_struct(weights: Dict[str, "object"]) -> BptLayerWeights:
     return BptLayerWeights(**{n: _ptr(weights.get(n)) for n in WEIGHT_NAMES})
 
 
+# ----------------------------------------------------------------- argument checks
+# The C ABI takes raw device pointers and trusts the sizes implied by the
+# descriptor, so a short, mistyped or strided tensor would make the kernels read
+# or write outside it. Every tensor is checked here before the library is
+# called; a failed check raises ValueError and launches nothing.
+DEVICE_TYPE = "cuda"
+_TORCH_DTYPE_NAMES = {0: "float32", 1: "bfloat16"}
+
+
+def weight_shapes_of(desc) -> Dict[str, tuple]:
+    """Shape of every weight the descriptor admits (w_3 only for SwiGLU;
+    norm shifts only for LayerNorm)."""
+    d = _desc(desc)
+    h, f, hd = d.hidden, d.ffn_dim, d.n_heads * d.head_dim
+    qkv = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim
+    shapes = {"w_qkv": (h, qkv), "b_qkv": (qkv,), "w_o": (hd, h), "b_o": (h,), "w_1": (h, f),
+              "b_1": (f,), "w_2": (f, h), "b_2": (h,), "n1_g": (h,), "n2_g": (h,)}
+    if d.ffn == FFNS["swiglu"]:
+        shapes["w_3"] = (h, f)
+    if d.norm == NORMS["layernorm"]:
+        shapes["n1_b"] = (h,)
+        shapes["n2_b"] = (h,)
+    return shapes
+
+
+def _check_tensor(t, name, device, dtype=None, numel=None, shape=None, min_bytes=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.device.type != DEVICE_TYPE:
+        raise ValueError(f"{name} must be a {DEVICE_TYPE} tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (got {t.numel()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_bytes}")
+
+
+def _check_weights(d, weights, device):
+    shapes = weight_shapes_of(d)
+    dt = _TORCH_DTYPE_NAMES[d.dtype]
+    unknown = set(weights) - set(WEIGHT_NAMES)
+    if unknown:
+        raise ValueError(f"unknown weight names {sorted(unknown)}")
+    for n in WEIGHT_NAMES:
+        t = weights.get(n)
+        if t is None:
+            continue
+        if n not in shapes:
+            raise ValueError(f"{n} is not used by this layer (must be absent)")
+        _check_tensor(t, n, device, dtype=dt, shape=shapes[n])
+
+
+def check_forward_args(desc, x, weights, y, saved, workspace) -> None:
+    """Raise ValueError unless every tensor matches the descriptor."""
+    d = _desc(desc)
+    if d.dtype not in _TORCH_DTYPE_NAMES:
+        raise ValueError("descriptor dtype")
+    n = d.batch * d.seq_len * d.hidden
+    dt = _TORCH_DTYPE_NAMES[d.dtype]
+    _check_tensor(x, "x", None, dtype=dt, numel=n)
+    dev = x.device
+    _check_tensor(y, "y", dev, dtype=dt, numel=n)
+    _check_weights(d, weights, dev)
+    _check_tensor(saved, "saved", dev, min_bytes=bpt_layer_saved_size(d))
+    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_layer_workspace_size(d, False))
+
+
+def check_backward_args(desc, x, weights, saved, dy, dx, grads, workspace) -> None:
+    """Raise ValueError unless every tensor matches the descriptor."""
+    d = _desc(desc)
+    if d.dtype not in _TORCH_DTYPE_NAMES:
+        raise ValueError("descriptor dtype")
+    n = d.batch * d.seq_len * d.hidden
+    dt = _TORCH_DTYPE_NAMES[d.dtype]
+    _check_tensor(x, "x", None, dtype=dt, numel=n)
+    dev = x.device
+    _check_tensor(dy, "dy", dev, dtype=dt, numel=n)
+    _check_tensor(dx, "dx", dev, dtype=dt, numel=n)
+    _check_weights(d, weights, dev)
+    _check_tensor(saved, "saved", dev, min_bytes=bpt_layer_saved_size(d))
+    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_layer_workspace_size(d, True))
+    shapes = weight_shapes_of(d)
+    unknown = set(grads) - set(GRAD_NAMES)
+    if unknown:
+        raise ValueError(f"unknown gradient names {sorted(unknown)}")
+    for g, t in grads.items():
+        if t is None:
+            continue
+        if g[1:] not in shapes:
+            raise ValueError(f"{g} is not used by this layer (must be absent)")
+        _check_tensor(t, g, dev, dtype="float32", shape=shapes[g[1:]])
+
+
 def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -221,8 +321,10 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def bpt_layer_forward(desc, x, weights, y, saved, workspace, stream=None) -> int:
-    """Raw call: every argument is a device tensor (weights: dict by name)."""
+    """Raw call: every argument is a device tensor (weights: dict by name),
+    checked against the descriptor first (ValueError, nothing launched)."""
     d = _desc(desc)
+    check_forward_args(d, x, weights, y, saved, workspace)
     w = _weights_struct(weights)
     return load_library().bpt_layer_forward(
         ctypes.byref(d), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(saved), _ptr(workspace),
@@ -231,8 +333,11 @@ def bpt_layer_forward(desc, x, weights, y, saved, workspace, stream=None) -> int
 
 def bpt_layer_backward(desc, x, weights, saved, dy, dx, grads, workspace, accumulate=False,
                        stream=None) -> int:
-    """Raw call: grads is a dict of fp32 device tensors by GRAD_NAMES (missing = not computed)."""
+    """Raw call: grads is a dict of fp32 device tensors by GRAD_NAMES (missing = not
+    computed); every tensor is checked against the descriptor first (ValueError, nothing
+    launched)."""
     d = _desc(desc)
+    check_backward_args(d, x, weights, saved, dy, dx, grads, workspace)
     w = _weights_struct(weights)
     g = BptLayerGrads(**{n: _ptr(grads.get(n)) for n in GRAD_NAMES}, accumulate=int(accumulate),
                       reserved=0)

@@ -7,14 +7,15 @@
 //   xn = Norm1(x)
 //   for each head chunk: Q, K, V of the chunk's heads (bias, RoPE) -> blockwise
 //                        attention -> O[:, chunk heads] and the per-row LSE
-//   for each query block i of q_block rows:
-//       h1 = x_i + O_i W_o + b_o            (fp32 block scratch)
-//       z  = Norm2(h1); u = act(z W_1 + b_1)  (q_block x ffn_dim scratch only)
-//       y_i = h1 + u W_2 + b_2
-// Backward per sequence: per query block, recompute h1, z, the FFN
-// pre-activation and u, then the FFN/Norm2/O-projection backward; then per
-// head chunk recompute Q, K, V and run the attention backward, the QKV weight
-// gradient and dxn; finally Norm1's backward plus the residual.
+//   h1 = x + O W_o + b_o                    (whole sequence, fp32 workspace)
+//   for each group of whole query blocks (at most min(8192, s/2) rows):
+//       z  = Norm2(h1_g); u = act(z W_1 + b_1)  (group x ffn_dim scratch only)
+//       y_g = h1_g + u W_2 + b_2
+// Backward per sequence: recompute h1; per group of query blocks recompute z,
+// the FFN pre-activation and u, then the FFN and Norm2 backward and the FFN
+// weight gradients; the O-projection backward over the whole sequence; then
+// per head chunk recompute Q, K, V and run the attention backward, the QKV
+// weight gradient and dxn; finally Norm1's backward plus the residual.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -96,15 +97,14 @@ struct TimedLaunch {
 
 constexpr int kColsumParts = 64;   // row splits of the bias-gradient column sums
 constexpr int kNormWaves = 2048;   // waves of the norm backward (partial rows)
-// Norm2 and the FFN (and in the backward their recompute and gradients) run
-// on groups of up to this many consecutive query blocks: GEMMs four times
-// taller, a quarter of the launches, and one read-modify-write of the fp32
-// dW_1 / dW_2 per group. The FFN scratch stays O(c_q f): no s x f term.
-// The FFN (forward and backward) runs over groups of consecutive query blocks
-// of about this many rows: the weight gradients reduce over a group's rows,
-// and at 8192 rows their GEMMs run near the speed of the sequence-long ones
-// while the scratch stays independent of s.
+// Norm2 and the FFN (forward, and in the backward their recompute and
+// gradients) run over groups of whole consecutive query blocks of at most
+// kFfnGroupRows rows and at most half the sequence (a single block of more
+// rows runs alone): GEMMs taller than one block, fewer launches, and one
+// read-modify-write of the fp32 dW_1 / dW_2 per group. The FFN scratch is one
+// group's rows x ffn_dim, never s x ffn_dim.
 constexpr int64_t kFfnGroupRows = 8192;
+constexpr int64_t kMaxHidden = 16384;  // widest row the norm kernels take
 constexpr int kDkvMaxParts = 4;  // query-head split of the dK/dV pass (see attn_bwd)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -139,7 +139,8 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
     return fail(BPT_EUNSUPPORTED, "fp32 mode supports head_dim 32 or 64");
   if (d->hidden != d->n_heads * d->head_dim)
     return fail(BPT_EINVAL, "hidden must equal n_heads * head_dim");
-  if (d->hidden % 64 != 0 || d->hidden > 65536) return fail(BPT_EINVAL, "hidden % 64");
+  if (d->hidden % 64 != 0) return fail(BPT_EINVAL, "hidden must be a multiple of 64");
+  if (d->hidden > kMaxHidden) return fail(BPT_EUNSUPPORTED, "hidden above 16384");
   if (d->ffn_dim < 64 || d->ffn_dim % 64 != 0 || d->ffn_dim > (1 << 20))
     return fail(BPT_EINVAL, "ffn_dim must be a positive multiple of 64");
   if (d->q_block < 8 || d->q_block % 8 != 0 || d->seq_len % d->q_block != 0)
@@ -160,7 +161,7 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
   p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
   p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
   p.chunk_cols = (p.U + 2 * p.nkvc) * p.D;
-  p.gq = std::min<int64_t>(p.s / p.cq, std::max<int64_t>(1, kFfnGroupRows / p.cq));
+  p.gq = std::max<int64_t>(1, std::min<int64_t>(p.s / p.cq / 2, kFfnGroupRows / p.cq));
   p.rope_base = d->rope_base; p.eps = d->norm_eps;
   p.esz = d->dtype == BPT_BF16 ? 2 : 4;
   return BPT_OK;
@@ -309,26 +310,29 @@ int device_cus() {
 }
 
 template <bool AK, bool BK, int BM, int BN, int BKK, int ST, int WM, int WN, int NW, class Epi>
-void launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
-                     int64_t M, int64_t N, int64_t K, const Epi& epi, int ksplit = 1) {
+bpt_status launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf16* B, int64_t ldb,
+                           int64_t M, int64_t N, int64_t K, const Epi& epi, int ksplit = 1) {
   constexpr int kLds = ST * (BM + BN) * BKK * 2;
   auto kern = gemm_dma_kernel<AK, BK, BM, BN, BKK, ST, WM, WN, NW, Epi>;
   // The dynamic-LDS limit is raised once per instantiation and device (a bit
-  // per device in `raised`; setting it twice from racing threads is harmless).
+  // per device in `raised`, set only once the call succeeded; setting it
+  // twice from racing threads is harmless).
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    const uint64_t bit = 1ull << dev;
-    if (!(raised.load(std::memory_order_acquire) & bit)) {
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-      raised.fetch_or(bit, std::memory_order_release);
-    }
-  } else {
-    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  const uint64_t bit = known ? 1ull << dev : 0;
+  if (!known || !(raised.load(std::memory_order_acquire) & bit)) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess)
+      return fail(BPT_EHIP, std::string("raising the GEMM's dynamic LDS limit: ") +
+                                hipGetErrorString(e));
+    if (known) raised.fetch_or(bit, std::memory_order_release);
   }
   const int64_t nt = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)(nt * ksplit)), dim3(64 * NW), kLds, st, A, lda, B, ldb,
                      (int)M, (int)N, (int)K, ksplit, epi);
+  return BPT_OK;
 }
 
 // kbuf (kbuf_floats fp32 elements of workspace), when given, lets a weight
@@ -367,8 +371,8 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
             ks /= 2;
           if (ks > 1) {
             EpiPart ep{kbuf, N, M * N};
-            launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, ep,
-                                                                 ks);
+            BPT_TRY((launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N,
+                                                                          K, ep, ks)));
             hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((M * N + 255) / 256)),
                                dim3(256), 0, st, kbuf, ks, (int)M, (int)N, epi);
             return check_launch(what);
@@ -376,12 +380,15 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
         }
       }
       if (nt256 >= device_cus()) {
-        launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K, epi);
+        BPT_TRY((launch_gemm_dma<AK, BK, 256, 256, 64, 2, 64, 128, 8>(st, A, lda, B, ldb, M, N, K,
+                                                                      epi)));
       } else if (K >= 32768) {
         // long reductions (weight gradients over the sequence): three stages
-        launch_gemm_dma<AK, BK, 128, 128, 64, 3, 64, 32, 8>(st, A, lda, B, ldb, M, N, K, epi);
+        BPT_TRY((launch_gemm_dma<AK, BK, 128, 128, 64, 3, 64, 32, 8>(st, A, lda, B, ldb, M, N, K,
+                                                                     epi)));
       } else {
-        launch_gemm_dma<AK, BK, 128, 128, 64, 2, 32, 64, 8>(st, A, lda, B, ldb, M, N, K, epi);
+        BPT_TRY((launch_gemm_dma<AK, BK, 128, 128, 64, 2, 32, 64, 8>(st, A, lda, B, ldb, M, N, K,
+                                                                     epi)));
       }
       return check_launch(what);
     }

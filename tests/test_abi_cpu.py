@@ -75,6 +75,8 @@ def _desc(name="gpt1b-s8k", **kw):
     d = bpt.LayerConfig.from_shape(wl.WORKLOADS[name]).desc()
     for k, v in kw.items():
         setattr(d, k, v)
+    if "hidden" in kw and "n_heads" not in kw and kw["hidden"] % d.head_dim == 0:
+        d.n_heads = d.n_kv_heads = d.head_chunk = kw["hidden"] // d.head_dim
     return d
 
 
@@ -93,6 +95,8 @@ def test_workloads_validate(name):
     ("seq_len", 8200, 1), ("seq_len", 0, 1), ("hidden", 2000, 1), ("n_kv_heads", 3, 1),
     ("head_dim", 96, 3), ("ffn_dim", 100, 1), ("q_block", 1000, 1), ("kv_block", 3000, 1),
     ("head_chunk", 3, 1), ("head_chunk", 0, 1), ("norm_eps", float("nan"), 1),
+    # the norm kernels take rows of at most 16384 elements
+    ("hidden", 32768, 3),
 ])
 def test_invalid_descriptors(field, value, status):
     d = _desc(**{field: value})
@@ -166,7 +170,7 @@ def test_memory_is_affine_in_s_without_s_times_ffn(backward):
         d3 = (sizes[3][i] - sizes[2][i]) / 4
         assert abs(d1 - d2) <= 4096 and abs(d2 - d3) <= 4096     # linear in s (alignment slack)
     # The FFN width changes the workspace by the same amount at every s: the
-    # FFN scratch is q_block x ffn_dim, never s x ffn_dim.
+    # FFN scratch covers one group of query blocks, never s x ffn_dim.
     df_small = ws(16384, 16384)[0] - ws(16384, 8192)[0]
     df_large = ws(131072, 16384)[0] - ws(131072, 8192)[0]
     assert df_small == df_large
@@ -216,3 +220,108 @@ def test_bench_refuses_more_than_one_gpu():
     assert proc.returncode != 0
     assert "one GPU" in proc.stderr
     assert proc.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("q_block", [512, 1024, 2048, 4096, 8192])
+def test_ffn_scratch_is_a_group_of_query_blocks(q_block):
+    """At s = 8192 the FFN scratch (the part of the backward workspace that
+    grows with ffn_dim: pre-activation, activation and its gradient, plus the
+    64 column-sum partial rows) covers one group of whole query blocks of at
+    most s / 2 rows; only a single query block spanning the sequence makes
+    it s rows ("Blockwise Parallel Transformer...", §3.2: the FFN runs per
+    query block)."""
+    base = wl.WORKLOADS["gpt1b-s8k"].replace(q_block=q_block)
+    s = base.seq_len
+
+    def ws(f):
+        return bpt.bpt_layer_workspace_size(
+            bpt.LayerConfig.from_shape(base.replace(ffn_dim=f)).desc(), True)
+
+    df = 8192
+    grow = ws(2 * df) - ws(df)
+    rows = s if q_block == s else s // 2
+    # three [rows, f] bf16 buffers (a, u, da) and 64 fp32 partial rows
+    assert grow <= 3 * rows * df * 2 + 64 * df * 4 + 3 * 256
+    if q_block < s:
+        assert grow < 3 * s * df * 2
+
+
+# ----------------------------------------------------------------- binding checks
+class _Stream:
+    cuda_stream = 0
+
+
+def _binding_args(torch, sh):
+    cfg = bpt.LayerConfig.from_shape(sh)
+    d = cfg.desc()
+    dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+    n = (sh.batch, sh.seq_len, sh.hidden)
+    w = {k: torch.zeros(s, dtype=dt) for k, s in wl.weight_shapes(sh).items()}
+    return dict(
+        d=d, x=torch.zeros(n, dtype=dt), y=torch.zeros(n, dtype=dt), dy=torch.zeros(n, dtype=dt),
+        dx=torch.zeros(n, dtype=dt), w=w,
+        saved=torch.zeros(bpt.bpt_layer_saved_size(d), dtype=torch.uint8),
+        wsf=torch.zeros(bpt.bpt_layer_workspace_size(d, False), dtype=torch.uint8),
+        wsb=torch.zeros(bpt.bpt_layer_workspace_size(d, True), dtype=torch.uint8),
+        grads={"d" + k: torch.zeros(s, dtype=torch.float32) for k, s in wl.weight_shapes(sh).items()})
+
+
+def _mutations(torch):
+    return {
+        "x-fp32-under-bf16": lambda a: a.update(x=a["x"].float()),
+        "x-transposed-view": lambda a: a.update(x=a["x"].transpose(1, 2).contiguous().transpose(1, 2)),
+        "y-short": lambda a: a.update(y=a["y"][:, :-1]),
+        "dy-short": lambda a: a.update(dy=a["dy"][:, :-16]),
+        "dx-wrong-dtype": lambda a: a.update(dx=a["dx"].float()),
+        "saved-short": lambda a: a.update(saved=a["saved"][:-1]),
+        "ws-short": lambda a: a.update(wsf=a["wsf"][:-1], wsb=a["wsb"][:-1]),
+        "w_o-short": lambda a: a["w"].update(w_o=a["w"]["w_o"][:-1]),
+        "w_1-transposed-shape": lambda a: a["w"].update(w_1=a["w"]["w_1"].t().contiguous()),
+        "w_qkv-wrong-dtype": lambda a: a["w"].update(w_qkv=a["w"]["w_qkv"].float()),
+        "rmsnorm-with-shift": lambda a: a["w"].update(n1_b=torch.zeros_like(a["w"]["n1_g"])),
+        "unknown-weight": lambda a: a["w"].update(w_9=a["w"]["w_1"]),
+        "grad-bf16": lambda a: a["grads"].update(dw_1=a["grads"]["dw_1"].bfloat16()),
+        "grad-wrong-shape": lambda a: a["grads"].update(dw_2=a["grads"]["dw_1"]),
+    }
+
+
+def _call(kind, a):
+    if kind == "forward":
+        return bpt.bpt_layer_forward(a["d"], a["x"], a["w"], a["y"], a["saved"], a["wsf"],
+                                     stream=_Stream())
+    return bpt.bpt_layer_backward(a["d"], a["x"], a["w"], a["saved"], a["dy"], a["dx"],
+                                  a["grads"], a["wsb"], stream=_Stream())
+
+
+@pytest.mark.parametrize("kind", ["forward", "backward"])
+def test_binding_checks_tensors_before_any_launch(kind, monkeypatch):
+    """The binding refuses tensors that do not match the descriptor (device,
+    dtype, contiguity, element count, weight and gradient shapes, saved and
+    workspace sizes) with ValueError and never reaches the library's compute
+    entry points, which would otherwise read or write outside the tensors."""
+    torch = pytest.importorskip("torch")
+    lib = bpt.load_library()
+    calls = []
+    monkeypatch.setattr(lib, "bpt_layer_forward", lambda *a: calls.append("f") or 0)
+    monkeypatch.setattr(lib, "bpt_layer_backward", lambda *a: calls.append("b") or 0)
+    sh = wl.SMALL["llama8b-small"]   # bf16, RMSNorm, SwiGLU, GQA
+    # Host tensors are refused outright (the library takes device pointers).
+    with pytest.raises(ValueError, match="cuda"):
+        _call(kind, _binding_args(torch, sh))
+    assert not calls
+    # With host tensors admitted, matching arguments reach the (stubbed) call.
+    monkeypatch.setattr(bpt, "DEVICE_TYPE", "cpu")
+    assert _call(kind, _binding_args(torch, sh)) == 0
+    assert calls == [kind[0]]
+    calls.clear()
+    relevant = {"forward": {"dy-short", "dx-wrong-dtype", "grad-bf16", "grad-wrong-shape"},
+                "backward": {"y-short"}}[kind]
+    for name, mutate in _mutations(torch).items():
+        if name in relevant:
+            continue
+        a = _binding_args(torch, sh)
+        mutate(a)
+        with pytest.raises(ValueError):
+            _call(kind, a)
+            pytest.fail(f"{name}: accepted")
+        assert not calls, name
