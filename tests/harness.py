@@ -13,6 +13,15 @@ import workloads as wl
 
 # Parity bars (relative L2 per tensor, computed in float64).
 TOL = {"f32": 1e-5, "bf16": 1e-2}
+# Local bars, as a multiple of the tensor bar: the error of every row of y and
+# dx (and of their non-residual parts), and of every 32 x 32 tile of a weight
+# gradient (32-element segment of a vector), divided by the norm an average
+# row / tile of the reference has (||ref|| * sqrt(block size / tensor size)).
+# A wrong row or tile has a local error of order one; for a single head's
+# attention tile feeding a row through the projections, about
+# 1 / sqrt(3 heads-worth of terms) or more, far above LOCAL_FACTOR x TOL.
+LOCAL_FACTOR = 5.0
+TILE = 32
 
 
 def rel_l2(got, ref) -> float:
@@ -23,6 +32,33 @@ def rel_l2(got, ref) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+def local_max(got, ref, rowwise: bool) -> float:
+    """Largest block error relative to the norm of an average reference block.
+    rowwise: blocks are the rows of [..., h] (y, dx); otherwise 32 x 32 tiles of
+    a matrix or 32-element segments of a vector (padded with zeros)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    if rowwise:
+        d2 = diff.reshape(-1, diff.shape[-1])
+        num = np.sqrt((d2 * d2).sum(axis=1))
+        nblk, bsz = d2.shape[0], d2.shape[1]
+    else:
+        if diff.ndim == 1:
+            diff = diff[None, :]
+        m, n = diff.shape
+        pm, pn = -m % TILE if m > 1 else 0, -n % TILE
+        dp = np.pad(diff, ((0, pm), (0, pn)))
+        bm = TILE if m > 1 else 1
+        blk = dp.reshape(dp.shape[0] // bm, bm, dp.shape[1] // TILE, TILE)
+        num = np.sqrt((blk * blk).sum(axis=(1, 3))).ravel()
+        nblk, bsz = num.size, bm * TILE
+    den = np.linalg.norm(ref) * np.sqrt(bsz / max(ref.size, 1))
+    if den == 0.0:
+        return 0.0 if num.max(initial=0.0) == 0.0 else float("inf")
+    return float(num.max(initial=0.0) / den)
 
 
 class Inputs:
@@ -88,18 +124,40 @@ def run_oracle(inp: Inputs, backward=True, rows=None):
     return orc.layer(x, w, sp, dy=dy, rows=rows)
 
 
-def compare(gpu, ref, dtype, rows=None, residual_x=None, dy=None):
-    """Per-tensor relative L2 of every output; returns {name: err}."""
+def compare(gpu, ref, dtype, rows=None, residual_x=None, dy=None, local=True):
+    """Per-tensor relative L2 of every output, {name: err}; with ``local``
+    also the largest row / tile error, under "name@row" / "name@tile"."""
     errs = {}
+
+    def put(name, got, want, rowwise):
+        errs[name] = rel_l2(got, want)
+        if local:
+            errs[name + ("@row" if rowwise else "@tile")] = local_max(got, want, rowwise)
+
     gy = gpu["y"] if rows is None else gpu["y"][:, rows]
-    errs["y"] = rel_l2(gy, ref["y"])
+    put("y", gy, ref["y"], True)
     if residual_x is not None:
         rx = residual_x if rows is None else residual_x[:, rows]
-        errs["y-x"] = rel_l2(gy - rx, ref["y"] - rx)
+        put("y-x", gy - rx, ref["y"] - rx, True)
     if "dx" in ref:
-        errs["dx"] = rel_l2(gpu["dx"], ref["dx"])
+        put("dx", gpu["dx"], ref["dx"], True)
         if dy is not None:
-            errs["dx-dy"] = rel_l2(gpu["dx"] - dy, ref["dx"] - dy)
+            put("dx-dy", gpu["dx"] - dy, ref["dx"] - dy, True)
         for k, v in ref["grads"].items():
-            errs["d" + k] = rel_l2(gpu["grads"][k], v)
+            put("d" + k, gpu["grads"][k], v, False)
     return errs
+
+
+def over_bar(errs, dtype, bars=None):
+    """{name: err} of every entry above its bar: TOL[dtype] per tensor,
+    LOCAL_FACTOR x that per row / tile; ``bars`` overrides the tensor bar by
+    name (the local bar follows it)."""
+    bad = {}
+    for k, v in errs.items():
+        base = k.split("@")[0]
+        bar = (bars or {}).get(base, TOL[dtype])
+        if "@" in k:
+            bar *= LOCAL_FACTOR
+        if not v <= bar:
+            bad[k] = (v, bar)
+    return bad

@@ -248,3 +248,13 @@ def sample_rows(sh: LayerShape, n_head: int = 8, n_tail: int = 8, n_mid: int = 8
                      replace=False)
     rows = np.concatenate([np.arange(min(n_head, s)), mid, np.arange(tail0, s - 1)])
     return np.unique(rows)
+
+
+def scaled(t: Tensor, factor: float, cols=slice(None)) -> Tensor:
+    """A copy of ``t`` with the columns ``cols`` of its last axis multiplied by
+    ``factor`` before rounding to the storage dtype (exact for a power of two).
+    Used to build stress inputs, e.g. peaked attention scores from larger
+    query projections."""
+    vals = t.f32.copy()
+    vals[..., cols] *= np.float32(factor)
+    return _make(vals, t.dtype)
