@@ -42,14 +42,30 @@ def model_flops(sh) -> dict:
     attn = 4 * d * H * attn_pairs(s, sh.causal)
     fwd = (lin + attn) * sh.batch
     pairs = attn_pairs(s, sh.causal) * sh.batch
-    # Algorithmic attention FLOPs per kernel: forward QK^T and PV (4d per
-    # visible pair and head); backward dV, dP, dK in the dK/dV pass (6d) and dQ
-    # in the dQ pass (2d). "hw_" adds the recomputed products each kernel runs.
     return {"fwd": fwd, "step": 3 * fwd,
-            "attn_fwd": 4 * d * H * pairs, "attn_bwd_dkdv": 6 * d * H * pairs,
-            "attn_bwd_dq": 2 * d * H * pairs,
-            "hw_attn_fwd": 4 * d * H * pairs, "hw_attn_bwd_dkdv": 8 * d * H * pairs,
-            "hw_attn_bwd_dq": 6 * d * H * pairs}
+            # attention units (see ROOFLINE_UNITS): forward QK^T and PV, 4d per
+            # visible pair and head; backward dV, dP, dK and dQ, 8d
+            "attn_fwd": 4 * d * H * pairs, "attn_bwd": 8 * d * H * pairs,
+            # what the kernels run, with the recomputed products: the forward
+            # 4d; dK/dV recomputes S (+2d); the dQ pass recomputes S and dP (+4d)
+            "hw_attn_fwd": 4 * d * H * pairs, "hw_attn_bwd": 14 * d * H * pairs}
+
+
+# Roofline units: the attention forward kernel alone, and the attention
+# backward as the pair of kernels it is split into (dK/dV pass, then dQ pass).
+ROOFLINE_UNITS = {"attn_fwd": ["attn_fwd"], "attn_bwd": ["attn_bwd_dkdv", "attn_bwd_dq"]}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def load_traffic(kernel: str, workload: str):
@@ -89,9 +105,74 @@ def cpu_baseline(sh, sample_len: int) -> dict:
     full = model_flops(sh)
     tokens_per_s = rate / (full["step"] / (sh.seq_len * sh.batch))
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"float64 oracle forward+backward of the same layer at s={sample_len} "
                        f"({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s); model-FLOP rate scaled to the "
                        f"per-token FLOPs at s={sh.seq_len}")}
+
+
+def _peak_activation_bytes(sh) -> dict:
+    """One forward + backward of the layer with torch-allocated saved buffer
+    and workspaces; returns the library's exact sizes and torch's peak
+    allocation above what was live before (inputs, weights, gradients, y, dx)."""
+    import numpy as np
+    import torch
+    import memory_efficient_long_amd as bpt
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(sh.batch, sh.seq_len, sh.hidden, device=dev, generator=gen).to(dt)
+    w = {k: (torch.randn(s, device=dev, generator=gen) * 0.02).to(dt)
+         for k, s in wl.weight_shapes(sh).items()}
+    dy = torch.randn_like(x)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    cfg = bpt.LayerConfig.from_shape(sh)
+    grads = {k: torch.empty(s, dtype=torch.float32, device=dev)
+             for k, s in bpt.grad_shapes(cfg, w).items()}
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    _, saved = bpt.forward(cfg, x, w, y=y)
+    bpt.backward(cfg, x, w, saved, dy, dx=dx, grads=grads)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    d = cfg.desc()
+    lib = (bpt.bpt_layer_saved_size(d) + max(bpt.bpt_layer_workspace_size(d, False),
+                                              bpt.bpt_layer_workspace_size(d, True)))
+    del saved, x, w, dy, y, dx, grads
+    torch.cuda.empty_cache()
+    return {"s": sh.seq_len, "head_chunk": sh.head_chunk, "library_bytes": lib,
+            "torch_peak_bytes": int(peak)}
+
+
+def memory_sweep() -> int:
+    """Peak activation memory over s at the GPT-1B shape (affine fit) and
+    over the head chunk at the Llama-8B shape."""
+    import numpy as np
+    import workloads as wl
+    base = wl.WORKLOADS["gpt1b-s128k"]
+    pts = []
+    for s in (16384, 32768, 65536, 131072):
+        print(f"[memory] gpt1b s={s}", file=sys.stderr, flush=True)
+        pts.append(_peak_activation_bytes(base.replace(seq_len=s)))
+    ss = np.array([p["s"] for p in pts], dtype=np.float64)
+    fit = {}
+    for key in ("library_bytes", "torch_peak_bytes"):
+        v = np.array([p[key] for p in pts], dtype=np.float64)
+        slope, icpt = np.polyfit(ss, v, 1)
+        resid = np.max(np.abs(v - (slope * ss + icpt)) / v)
+        fit[key] = {"bytes_per_token": round(slope, 1),
+                    "sbh_per_token": round(slope / base.hidden, 3),
+                    "intercept_bytes": round(icpt), "max_rel_residual": float(resid)}
+    chunks = []
+    llama = wl.WORKLOADS["llama8b-s64k"]
+    for u in (4, 8, 16, 32):
+        print(f"[memory] llama8b head_chunk={u}", file=sys.stderr, flush=True)
+        chunks.append(_peak_activation_bytes(llama.replace(head_chunk=u)))
+    print(json.dumps({"memory_sweep": {"gpt1b": pts, "affine_fit": fit,
+                                       "llama8b_head_chunk": chunks}}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -106,6 +187,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="only measure peak activation bytes over s (GPT-1B shape) and head chunk "
+                         "(Llama-8B shape) and print one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -130,9 +214,12 @@ def main() -> int:
     import torch
 
     import memory_efficient_long_amd as bpt
+    from memory_efficient_long_amd import accounting as acc
     import workloads as wl
 
     bpt.load_library()
+    if args.memory_sweep:
+        return memory_sweep()
     sh = wl.WORKLOADS[args.workload]
     if args.head_chunk:
         sh = sh.replace(head_chunk=args.head_chunk)
@@ -212,27 +299,38 @@ def main() -> int:
     tflops = fl["step"] / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
 
-    # Dominant kernel: the attention kernel with the largest measured time.
-    dom = max(attn_classes, key=lambda c: timing[c][0])
-    dom_ms, dom_n = timing[dom]
-    avg_ms = dom_ms / max(dom_n, 1)
-    per_launch_flops = fl[dom] / max(dom_n / args.steps, 1)
+    # Dominant unit: the attention forward kernel or the backward pair, by
+    # measured time. achieved = the unit's algorithmic FLOPs per launch over
+    # the sum of its kernels' average launch durations (HIP events on the
+    # launch stream, recorded by the library around each launch).
+    unit_ms = {u: sum(timing[c][0] for c in cs) for u, cs in ROOFLINE_UNITS.items()}
+    dom = max(unit_ms, key=unit_ms.get)
+    kernels = ROOFLINE_UNITS[dom]
+    launches = timing[kernels[0]][1] / args.steps          # launches of the unit per step
+    avg = {c: timing[c][0] / max(timing[c][1], 1) for c in kernels}
+    avg_ms = sum(avg.values())
+    per_launch_flops = fl[dom] / max(launches, 1)
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
     # bf16 with head_dim 64 / 128 runs the direct-to-LDS attention kernels.
     dma = sh.dtype == "bf16" and sh.head_dim in (64, 128)
-    kernel_name = dom + ("_dma_kernel" if dma else "_kernel")
-    traffic = (load_traffic(kernel_name, sh.name)
-               if sh.head_chunk == wl.WORKLOADS[args.workload].head_chunk else None)
+    names = {c: c + ("_dma_kernel" if dma else "_kernel") for c in kernels}
+    traffic = None
+    if sh.head_chunk == wl.WORKLOADS[args.workload].head_chunk:  # counters at the default chunk
+        parts = [load_traffic(names[c], sh.name) for c in kernels]
+        traffic = sum(parts) if all(v is not None for v in parts) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                # counters are taken at the workload's own head chunk
                 "traffic": traffic,
                 "traffic_gb_per_s": (round(traffic / (avg_ms * 1e-3) / 1e9, 1)
                                      if traffic and avg_ms > 0 else None),
-                "kernel": kernel_name,
-                "avg_launch_ms": round(avg_ms, 3), "launches_per_step": dom_n / args.steps,
+                "kernel": " + ".join(names[c] for c in kernels),
+                "avg_launch_ms": round(avg_ms, 3),
+                "kernel_avg_launch_ms": {names[c]: round(avg[c], 3) for c in kernels},
+                "launches_per_step": launches,
+                "flops_unit": ("4*d per visible (query, key) pair and head" if dom == "attn_fwd"
+                               else "8*d per visible (query, key) pair and head"),
                 "algorithmic_flops_per_launch": per_launch_flops,
-                "hardware_flops_per_launch": fl["hw_" + dom] / max(dom_n / args.steps, 1)}
+                "hardware_flops_per_launch": fl["hw_" + dom] / max(launches, 1)}
 
     breakdown = {c: {"ms_per_step": round(v[0] / args.steps, 3), "launches_per_step": v[1] / args.steps}
                  for c, v in timing.items() if v[1]}
@@ -267,7 +365,9 @@ def main() -> int:
                    "saved_sbh": round(saved_bytes / (tokens * sh.hidden), 3),
                    "peak_bytes_per_token": (saved_bytes + max(ws_f_bytes, ws_b_bytes)) / tokens,
                    "peak_sbh": round((saved_bytes + max(ws_f_bytes, ws_b_bytes)) / (tokens * sh.hidden), 3),
-                   "pages_bpt_sbh": 2, "pages_flashattention_ffn_sbh": 8,
+                   # the pages' per-layer predictions at this shape, in sbh
+                   "pages_sbh": {k: round(acc.sbh_per_layer(sh.hidden, sh.n_heads, sh.seq_len, k), 2)
+                                 for k in ("bpt", "flash", "vanilla")},
                    # cross-check: everything this process allocated on the GPU
                    # (inputs, weights, gradients, saved state, workspaces)
                    "torch_max_allocated_bytes": int(torch.cuda.max_memory_allocated(dev))},
