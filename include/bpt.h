@@ -145,6 +145,25 @@ bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x,
                              const bpt_layer_weights* w, void* y, void* saved, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same computation, arguments (minus the
+ * workspace) and results as bpt_layer_forward. Its workspace is a static
+ * device array of bpt_layer_noalloc_scratch_bytes() bytes (64 MiB) inside the
+ * library, one per GPU, held until the process ends; it calls no hipMalloc,
+ * hipFree or other allocating routine. A layer whose forward workspace
+ * (bpt_layer_workspace_size(desc, 0)) exceeds it returns BPT_EWORKSPACE
+ * before any launch. Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other host threads) race and must
+ * be serialised by the caller. The array keeps the last call's contents; the
+ * forward writes every scratch element before reading it. */
+bpt_status bpt_layer_forward_noalloc(const bpt_layer_desc* desc, const void* x,
+                                     const bpt_layer_weights* w, void* y, void* saved,
+                                     void* stream);
+
+/* Size in bytes of the static scratch of bpt_layer_forward_noalloc. */
+size_t bpt_layer_noalloc_scratch_bytes(void);
+
 /* Recompute-based backward ("Blockwise Parallel Transformer...", §3.4 memory analysis: the
  * backward recomputes blockwise; "Training memory...", §2 per-operation gradient rules and §3
  * FlashAttention backward from O and the log-sum-exp). x: the forward's input; saved: the

@@ -21,6 +21,7 @@ __all__ = [
     "forward", "backward", "WEIGHT_NAMES", "GRAD_NAMES", "bpt_timing_enable", "bpt_timing_read",
     "bpt_mfma_peak_probe",
     "KERNEL_CLASSES", "check_forward_args", "check_backward_args", "weight_shapes_of",
+    "bpt_layer_forward_noalloc", "bpt_layer_noalloc_scratch_bytes",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +97,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                        P(BptLayerGrads), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
     lib.bpt_layer_backward.restype = ctypes.c_int
+    lib.bpt_layer_forward_noalloc.argtypes = [P(BptLayerDesc), ctypes.c_void_p,
+                                              P(BptLayerWeights), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+    lib.bpt_layer_forward_noalloc.restype = ctypes.c_int
+    lib.bpt_layer_noalloc_scratch_bytes.argtypes = []
+    lib.bpt_layer_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.bpt_status_string.argtypes = [ctypes.c_int]
     lib.bpt_status_string.restype = ctypes.c_char_p
     lib.bpt_last_error.argtypes = []
@@ -272,7 +279,7 @@ def _check_weights(d, weights, device):
         _check_tensor(t, n, device, dtype=dt, shape=shapes[n])
 
 
-def check_forward_args(desc, x, weights, y, saved, workspace) -> None:
+def check_forward_args(desc, x, weights, y, saved, workspace, need_workspace=True) -> None:
     """Raise ValueError unless every tensor matches the descriptor."""
     d = _desc(desc)
     if d.dtype not in _TORCH_DTYPE_NAMES:
@@ -284,7 +291,8 @@ def check_forward_args(desc, x, weights, y, saved, workspace) -> None:
     _check_tensor(y, "y", dev, dtype=dt, numel=n)
     _check_weights(d, weights, dev)
     _check_tensor(saved, "saved", dev, min_bytes=bpt_layer_saved_size(d))
-    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_layer_workspace_size(d, False))
+    if need_workspace:
+        _check_tensor(workspace, "workspace", dev, min_bytes=bpt_layer_workspace_size(d, False))
 
 
 def check_backward_args(desc, x, weights, saved, dy, dx, grads, workspace) -> None:
@@ -329,6 +337,20 @@ def bpt_layer_forward(desc, x, weights, y, saved, workspace, stream=None) -> int
     return load_library().bpt_layer_forward(
         ctypes.byref(d), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(saved), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def bpt_layer_forward_noalloc(desc, x, weights, y, saved, stream=None) -> int:
+    """Raw call of the allocation-free forward (the library's static scratch
+    replaces the workspace); tensors are checked as for bpt_layer_forward."""
+    d = _desc(desc)
+    check_forward_args(d, x, weights, y, saved, None, need_workspace=False)
+    w = _weights_struct(weights)
+    return load_library().bpt_layer_forward_noalloc(
+        ctypes.byref(d), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(saved), _stream_handle(stream))
+
+
+def bpt_layer_noalloc_scratch_bytes() -> int:
+    return load_library().bpt_layer_noalloc_scratch_bytes()
 
 
 def bpt_layer_backward(desc, x, weights, saved, dy, dx, grads, workspace, accumulate=False,

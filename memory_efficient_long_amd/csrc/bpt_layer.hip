@@ -877,6 +877,37 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
+// ----------------------------------------------------------------- static scratch
+// Workspace of the allocation-free forward (bpt_layer_forward_noalloc): a
+// device array in the library's code object, so every GPU the library runs on
+// holds its own copy for the life of the process. Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and cached.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+bpt_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BPT_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BPT_EUNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(BPT_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BPT_OK;
+}
+
 bpt_status check_weights(const Plan& p, const bpt_layer_weights* w) {
   if (!w) return fail(BPT_EINVAL, "weights is NULL");
   const void* mats[4] = {w->w_qkv, w->w_o, w->w_1, w->w_2};
@@ -930,6 +961,32 @@ bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x, const bp
     return forward_impl<bf16>(p, (const bf16*)x, w, (bf16*)y, saved, ws, st);
   return forward_impl<float>(p, (const float*)x, w, (float*)y, saved, ws, st);
 }
+
+bpt_status bpt_layer_forward_noalloc(const bpt_layer_desc* desc, const void* x,
+                                     const bpt_layer_weights* w, void* y, void* saved,
+                                     void* stream) {
+  g_last_error.clear();
+  Plan p;
+  BPT_TRY(make_plan(desc, p));
+  BPT_TRY(check_weights(p, w));
+  if (!x || !y || !saved) return fail(BPT_EINVAL, "x, y and saved must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(saved))
+    return fail(BPT_EINVAL, "x, y and saved must be 16-byte aligned");
+  const size_t need = fwd_ws_bytes(p);
+  if (need > kScratchBytes)
+    return fail(BPT_EWORKSPACE, "this layer's forward needs " + std::to_string(need) +
+                                    " bytes of scratch; the static scratch holds " +
+                                    std::to_string(kScratchBytes) +
+                                    " (use bpt_layer_forward with a workspace)");
+  void* ws = nullptr;
+  BPT_TRY(scratch_address(&ws));
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return forward_impl<bf16>(p, (const bf16*)x, w, (bf16*)y, saved, ws, st);
+  return forward_impl<float>(p, (const float*)x, w, (float*)y, saved, ws, st);
+}
+
+size_t bpt_layer_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x, const bpt_layer_weights* w,
                               const void* saved, const void* dy, void* dx,

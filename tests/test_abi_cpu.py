@@ -325,3 +325,22 @@ def test_binding_checks_tensors_before_any_launch(kind, monkeypatch):
             _call(kind, a)
             pytest.fail(f"{name}: accepted")
         assert not calls, name
+
+
+def test_noalloc_forward_refuses_layers_beyond_its_scratch():
+    """The allocation-free forward checks its static scratch size on the host
+    and returns BPT_EWORKSPACE before any device work (the GPT-1B-shaped layer
+    at s = 8192 needs more than the 64 MiB it holds)."""
+    lib = bpt.load_library()
+    d = _desc()
+    assert bpt.bpt_layer_workspace_size(d, False) > bpt.bpt_layer_noalloc_scratch_bytes()
+    assert bpt.bpt_layer_noalloc_scratch_bytes() == 64 << 20
+    w = bpt.BptLayerWeights(w_qkv=0x1000, w_o=0x1000, w_1=0x1000, w_2=0x1000, n1_g=0x1000,
+                            n2_g=0x1000)
+    fake = 0x10000
+    assert lib.bpt_layer_forward_noalloc(ctypes.byref(d), fake, ctypes.byref(w), fake, fake,
+                                         None) == 2
+    assert "static scratch" in bpt.bpt_last_error()
+    # argument errors come first, as in bpt_layer_forward
+    assert lib.bpt_layer_forward_noalloc(ctypes.byref(d), None, ctypes.byref(w), fake, fake,
+                                         None) == 1
