@@ -175,6 +175,112 @@ def memory_sweep() -> int:
     return 0
 
 
+def bench_lm_head(args) -> int:
+    """One step = LM-head forward (loss) + backward (dz, dW_head) over all rows,
+    inputs resident in HBM."""
+    import numpy as np
+    import torch
+    import memory_efficient_long_amd as bpt
+    import workloads as wl
+    sh = wl.LM_HEADS[args.workload]
+    dev = torch.device("cuda:0")
+
+    def to_dev(t):
+        if t.dtype == "bf16":
+            return torch.from_numpy(t.storage.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(t.storage).to(dev)
+
+    cfg = bpt.LmHeadConfig(sh.rows, sh.hidden, sh.vocab, sh.chunk_rows, sh.dtype)
+    d = cfg.desc()
+    z, w = to_dev(wl.make_z(sh)), to_dev(wl.make_w_head(sh))
+    t = torch.from_numpy(wl.make_targets(sh)).to(dev)
+    valid = max(int((t >= 0).sum()), 1)
+    g = torch.full((sh.rows,), 1.0 / valid, dtype=torch.float32, device=dev)  # mean loss
+    loss = torch.empty(sh.rows, dtype=torch.float32, device=dev)
+    saved = torch.empty(bpt.bpt_lm_head_saved_size(d), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(bpt.bpt_lm_head_workspace_size(d, False), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bpt.bpt_lm_head_workspace_size(d, True), dtype=torch.uint8, device=dev)
+    dz = torch.empty_like(z)
+    dw = torch.empty(sh.hidden, sh.vocab, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = bpt.bpt_lm_head_forward(d, z, w, t, loss, saved, wsf, stream)
+        st = st or bpt.bpt_lm_head_backward(d, z, w, t, saved, g, dz, dw, wsb, False, stream)
+        if st:
+            raise bpt.BptError(st, "lm head")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    bpt.bpt_timing_enable(["lm_head", "rowwise"])
+    bpt.bpt_timing_read(reset=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    timing = bpt.bpt_timing_read(reset=True)
+    bpt.bpt_timing_enable([])
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.mean(step_ms))
+    n, h, V = sh.rows, sh.hidden, sh.vocab
+    model = 6 * n * h * V          # logits, dz and dW products (2nhV each)
+    hw = 8 * n * h * V             # + the logits recomputed in the backward
+    gm, gn = timing["lm_head"]
+    achieved = model / args.steps / (gm / args.steps * 1e-3) / 1e12 if gm > 0 else 0.0
+    peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {
+        "metric": "blockwise LM head + cross-entropy fwd+bwd tokens/s",
+        "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
+        "data": "synthetic",
+        "config": {"workload": sh.name, "rows": n, "hidden": h, "vocab": V,
+                   "chunk_rows": sh.chunk_rows},
+        "model_tflops": round(model / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "gemm_dma_kernel (LM head: logits with the log-sum-exp epilogue, "
+                               "recomputed logits with the dlogit epilogue, dz, dW)",
+                     "avg_launch_ms": round(gm / max(gn, 1), 3),
+                     "launches_per_step": gn / args.steps,
+                     "kernel_ms_per_step": round(gm / args.steps, 3),
+                     "flops_unit": "6*h*V per row (model); 8*h*V per row run (logits recomputed)",
+                     "hardware_flops_per_step": hw},
+        "rowwise_ms_per_step": round(timing["rowwise"][0] / args.steps, 3),
+        "memory": {"saved_bytes_per_token": bpt.bpt_lm_head_saved_size(d) / n,
+                   "workspace_bytes": max(wsf.numel(), wsb.numel()),
+                   "logits_fp32_bytes_not_held": 4 * n * V},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import lm_head_oracle as lmo
+        rows = min(n, 2048)
+        samp = sh.replace(rows=rows)
+        zz, ww = wl.make_z(samp).f64(), wl.make_w_head(samp).f64()
+        tt = wl.make_targets(samp)
+        gg = np.full(rows, 1.0 / rows)
+        t0 = time.perf_counter()
+        lmo.lm_head_ce(zz, ww, tt, gg)
+        dt = time.perf_counter() - t0
+        try:
+            import threadpoolctl
+            threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        out["cpu_baseline"] = {"value": rows / dt, "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": f"float64 oracle forward+backward on the first {rows} "
+                                         f"rows ({dt:.1f} s); rows are independent, so the rate "
+                                         f"is per row"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +326,8 @@ def main() -> int:
     bpt.load_library()
     if args.memory_sweep:
         return memory_sweep()
+    if args.workload in wl.LM_HEADS:
+        return bench_lm_head(args)
     sh = wl.WORKLOADS[args.workload]
     if args.head_chunk:
         sh = sh.replace(head_chunk=args.head_chunk)

@@ -180,6 +180,54 @@ bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x,
 /* Static description of a status code (never NULL). */
 const char* bpt_status_string(bpt_status status);
 
+/* ---- Blockwise LM head with cross-entropy loss ----
+ * "Blockwise Parallel Transformer for Long Context Large Models", §3.4 (handling of the
+ * cross-entropy loss: blockwise evaluation never holds all positions' logits) and "Training
+ * memory...", §3 (the logits, 4sbV bytes in fp32): for each row i of z [rows, hidden],
+ *   logits_i = z_i W_head,  loss_i = logsumexp(logits_i) - logits_i[t_i],
+ * with the log-sum-exp in fp32; a target outside [0, vocab) marks an ignored row (loss 0, no
+ * gradient). Rows run in chunks of chunk_rows: the forward reduces each chunk's logits inside
+ * the GEMM's epilogue to per-row log-sum-exp partials (nothing of size rows x vocab is
+ * written); the backward recomputes a chunk's logits and holds only that chunk's
+ * dlogits = g_i (softmax_i - onehot(t_i)) [chunk_rows, vocab] before dz = dlogits W_head^T
+ * and dW_head += z^T dlogits. */
+typedef struct {
+  int32_t abi_version; /* = BPT_ABI_VERSION */
+  int32_t dtype;       /* bpt_dtype of z, w_head and dz (losses, dloss, dw_head: fp32) */
+  int64_t rows;        /* positions (batch x sequence) */
+  int64_t hidden;      /* h, multiple of 64 */
+  int64_t vocab;       /* V, multiple of 64 (pad the vocabulary) */
+  int64_t chunk_rows;  /* rows per chunk, multiple of 64; chunk_rows x vocab < 2^31 */
+} bpt_lm_head_desc;
+
+/* Host-only check of an LM-head descriptor (the rules above). */
+bpt_status bpt_lm_head_validate(const bpt_lm_head_desc* desc);
+
+/* Bytes of the forward->backward state: one fp32 (base-2) log-sum-exp per row. */
+size_t bpt_lm_head_saved_size(const bpt_lm_head_desc* desc);
+
+/* Workspace bytes: forward (backward = 0) chunk_rows x (vocab / 32) (max, sum) pairs plus
+ * chunk_rows floats; backward (1) chunk_rows x vocab dlogits in the storage dtype. Independent
+ * of rows. Returns 0 for an invalid descriptor. */
+size_t bpt_lm_head_workspace_size(const bpt_lm_head_desc* desc, int32_t backward);
+
+/* Forward. z: [rows, hidden] (16-byte aligned); w_head: [hidden, vocab] (16-byte aligned);
+ * targets: int32 [rows]; loss: fp32 [rows] written (the per-row loss; sum or average it as
+ * needed); saved: bpt_lm_head_saved_size bytes written; ws: workspace (256-byte aligned). All
+ * device pointers, asynchronous on `stream`. Same error behaviour as bpt_layer_forward. */
+bpt_status bpt_lm_head_forward(const bpt_lm_head_desc* desc, const void* z, const void* w_head,
+                               const int32_t* targets, float* loss, void* saved, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Backward from dloss: fp32 [rows], the cotangent of each row's loss (e.g. 1 / number of
+ * counted rows for a mean). dz: [rows, hidden] in the storage dtype, overwritten; dw_head:
+ * fp32 [hidden, vocab], overwritten (accumulate = 0) or added to (1); either may be NULL (not
+ * computed), not both. saved: the forward's saved buffer. */
+bpt_status bpt_lm_head_backward(const bpt_lm_head_desc* desc, const void* z, const void* w_head,
+                                const int32_t* targets, const void* saved, const float* dloss,
+                                void* dz, float* dw_head, int32_t accumulate, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* ---- Kernel timing (instrumentation for benchmarks and profiling) ----
  * When a class is enabled, every launch of that kernel class is bracketed by
  * HIP events recorded on the same stream; bpt_timing_read() waits for the
@@ -193,7 +241,8 @@ typedef enum {
   BPT_KERNEL_ATTN_BWD_DQ = 2,  /* attention backward, dQ pass                     */
   BPT_KERNEL_GEMM = 3,         /* projections and FFN GEMMs with fused epilogues  */
   BPT_KERNEL_ROWWISE = 4,      /* norms, reductions, RoPE table, fills, D = rowsum */
-  BPT_KERNEL_CLASSES = 5
+  BPT_KERNEL_LM_HEAD = 5,      /* GEMMs of the LM head (logits, dz, dW_head)      */
+  BPT_KERNEL_CLASSES = 6
 } bpt_kernel_class;
 
 /* Enable timing for the classes whose bit (1 << class) is set; 0 disables. */

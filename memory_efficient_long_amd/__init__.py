@@ -22,6 +22,9 @@ __all__ = [
     "bpt_mfma_peak_probe",
     "KERNEL_CLASSES", "check_forward_args", "check_backward_args", "weight_shapes_of",
     "bpt_layer_forward_noalloc", "bpt_layer_noalloc_scratch_bytes",
+    "LmHeadConfig", "BptLmHeadDesc", "bpt_lm_head_validate", "bpt_lm_head_saved_size",
+    "bpt_lm_head_workspace_size", "bpt_lm_head_forward", "bpt_lm_head_backward",
+    "lm_head_forward", "lm_head_backward", "check_lm_head_args",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +60,12 @@ class BptLayerWeights(ctypes.Structure):
 class BptLayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES] + [
         ("accumulate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class BptLmHeadDesc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("hidden", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("chunk_rows", ctypes.c_int64)]
 
 
 class BptError(RuntimeError):
@@ -103,6 +112,19 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bpt_layer_forward_noalloc.restype = ctypes.c_int
     lib.bpt_layer_noalloc_scratch_bytes.argtypes = []
     lib.bpt_layer_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    LP = P(BptLmHeadDesc)
+    lib.bpt_lm_head_validate.argtypes = [LP]
+    lib.bpt_lm_head_validate.restype = ctypes.c_int
+    lib.bpt_lm_head_saved_size.argtypes = [LP]
+    lib.bpt_lm_head_saved_size.restype = ctypes.c_size_t
+    lib.bpt_lm_head_workspace_size.argtypes = [LP, ctypes.c_int32]
+    lib.bpt_lm_head_workspace_size.restype = ctypes.c_size_t
+    vp = ctypes.c_void_p
+    lib.bpt_lm_head_forward.argtypes = [LP, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bpt_lm_head_forward.restype = ctypes.c_int
+    lib.bpt_lm_head_backward.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                         ctypes.c_size_t, vp]
+    lib.bpt_lm_head_backward.restype = ctypes.c_int
     lib.bpt_status_string.argtypes = [ctypes.c_int]
     lib.bpt_status_string.restype = ctypes.c_char_p
     lib.bpt_last_error.argtypes = []
@@ -185,7 +207,7 @@ def bpt_last_error() -> str:
     return load_library().bpt_last_error().decode()
 
 
-KERNEL_CLASSES = ["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm", "rowwise"]
+KERNEL_CLASSES = ["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm", "rowwise", "lm_head"]
 
 
 def bpt_timing_enable(classes) -> int:
@@ -414,3 +436,113 @@ def backward(cfg: LayerConfig, x, weights, saved, dy, dx=None, grads=None, works
     if st:
         raise BptError(st, "bpt_layer_backward")
     return dx, grads
+
+
+# ----------------------------------------------------------------- LM head with cross-entropy
+@dataclasses.dataclass(frozen=True)
+class LmHeadConfig:
+    """Shape of the blockwise LM head (mirrors bpt_lm_head_desc)."""
+    rows: int
+    hidden: int
+    vocab: int
+    chunk_rows: int = 8192
+    dtype: str = "bf16"
+
+    def desc(self) -> BptLmHeadDesc:
+        return BptLmHeadDesc(abi_version=ABI_VERSION, dtype=DTYPES[self.dtype], rows=self.rows,
+                             hidden=self.hidden, vocab=self.vocab, chunk_rows=self.chunk_rows)
+
+
+def _lm_desc(d) -> BptLmHeadDesc:
+    return d.desc() if isinstance(d, LmHeadConfig) else d
+
+
+def bpt_lm_head_validate(desc) -> int:
+    return load_library().bpt_lm_head_validate(ctypes.byref(_lm_desc(desc)))
+
+
+def bpt_lm_head_saved_size(desc) -> int:
+    return load_library().bpt_lm_head_saved_size(ctypes.byref(_lm_desc(desc)))
+
+
+def bpt_lm_head_workspace_size(desc, backward: bool) -> int:
+    return load_library().bpt_lm_head_workspace_size(ctypes.byref(_lm_desc(desc)), int(backward))
+
+
+def check_lm_head_args(desc, z, w_head, targets, saved, workspace, backward, loss=None,
+                       dloss=None, dz=None, dw_head=None) -> None:
+    """Raise ValueError unless every tensor matches the LM-head descriptor."""
+    d = _lm_desc(desc)
+    if d.dtype not in _TORCH_DTYPE_NAMES:
+        raise ValueError("descriptor dtype")
+    dt = _TORCH_DTYPE_NAMES[d.dtype]
+    _check_tensor(z, "z", None, dtype=dt, numel=d.rows * d.hidden)
+    dev = z.device
+    _check_tensor(w_head, "w_head", dev, dtype=dt, shape=(d.hidden, d.vocab))
+    _check_tensor(targets, "targets", dev, dtype="int32", numel=d.rows)
+    _check_tensor(saved, "saved", dev, min_bytes=bpt_lm_head_saved_size(d))
+    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_lm_head_workspace_size(d, backward))
+    if not backward:
+        _check_tensor(loss, "loss", dev, dtype="float32", numel=d.rows)
+        return
+    _check_tensor(dloss, "dloss", dev, dtype="float32", numel=d.rows)
+    if dz is None and dw_head is None:
+        raise ValueError("dz and dw_head are both None")
+    if dz is not None:
+        _check_tensor(dz, "dz", dev, dtype=dt, numel=d.rows * d.hidden)
+    if dw_head is not None:
+        _check_tensor(dw_head, "dw_head", dev, dtype="float32", shape=(d.hidden, d.vocab))
+
+
+def bpt_lm_head_forward(desc, z, w_head, targets, loss, saved, workspace, stream=None) -> int:
+    """Raw call (device tensors, checked first)."""
+    d = _lm_desc(desc)
+    check_lm_head_args(d, z, w_head, targets, saved, workspace, False, loss=loss)
+    return load_library().bpt_lm_head_forward(
+        ctypes.byref(d), _ptr(z), _ptr(w_head), _ptr(targets), _ptr(loss), _ptr(saved),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def bpt_lm_head_backward(desc, z, w_head, targets, saved, dloss, dz, dw_head, workspace,
+                         accumulate=False, stream=None) -> int:
+    """Raw call (device tensors, checked first); dz or dw_head may be None."""
+    d = _lm_desc(desc)
+    check_lm_head_args(d, z, w_head, targets, saved, workspace, True, dloss=dloss, dz=dz,
+                       dw_head=dw_head)
+    return load_library().bpt_lm_head_backward(
+        ctypes.byref(d), _ptr(z), _ptr(w_head), _ptr(targets), _ptr(saved), _ptr(dloss), _ptr(dz),
+        _ptr(dw_head), int(accumulate), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def lm_head_forward(cfg: LmHeadConfig, z, w_head, targets, stream=None):
+    """loss, saved = lm_head_forward(cfg, z, w_head, targets): allocates outputs."""
+    import torch
+    d = cfg.desc()
+    st = bpt_lm_head_validate(d)
+    if st:
+        raise BptError(st, "bpt_lm_head_validate")
+    loss = torch.empty(cfg.rows, dtype=torch.float32, device=z.device)
+    saved = _alloc_bytes(bpt_lm_head_saved_size(d), z.device)
+    ws = _alloc_bytes(bpt_lm_head_workspace_size(d, False), z.device)
+    st = bpt_lm_head_forward(d, z, w_head, targets, loss, saved, ws, stream)
+    if st:
+        raise BptError(st, "bpt_lm_head_forward")
+    return loss, saved
+
+
+def lm_head_backward(cfg: LmHeadConfig, z, w_head, targets, saved, dloss, dz=None, dw_head=None,
+                     accumulate=False, stream=None):
+    """dz, dw_head = lm_head_backward(...): allocates what is not passed."""
+    import torch
+    d = cfg.desc()
+    if dz is None:
+        dz = torch.empty_like(z)
+    if dw_head is None:
+        dw_head = torch.empty(cfg.hidden, cfg.vocab, dtype=torch.float32, device=z.device)
+    ws = _alloc_bytes(bpt_lm_head_workspace_size(d, True), z.device)
+    st = bpt_lm_head_backward(d, z, w_head, targets, saved, dloss, dz, dw_head, ws, accumulate,
+                              stream)
+    if st:
+        raise BptError(st, "bpt_lm_head_backward")
+    return dz, dw_head

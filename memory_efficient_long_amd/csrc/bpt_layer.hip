@@ -32,6 +32,7 @@
 #include "gemm_dma.hpp"
 #include "peak.hpp"
 #include "gemm.hpp"
+#include "lm_head.hpp"
 #include "rowwise.hpp"
 
 using namespace bpt;
@@ -343,7 +344,7 @@ bpt_status launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf1
 template <typename T, bool AK, bool BK, class Epi>
 bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
                 int64_t N, int64_t K, const Epi& epi, const char* what, float* kbuf = nullptr,
-                int64_t kbuf_floats = 0) {
+                int64_t kbuf_floats = 0, int cls = BPT_KERNEL_GEMM) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int BKK = sizeof(T) == 2 ? 64 : 32;
   // Layout invariants of the tile loaders (16-byte vectors along the
@@ -355,7 +356,7 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
        (ldb % VEC == 0);
   if (!ok) return fail(BPT_EUNSUPPORTED, std::string("gemm layout invariant: ") + what);
   if (M == 0 || N == 0) return BPT_OK;
-  TimedLaunch tl(BPT_KERNEL_GEMM, st);
+  TimedLaunch tl(cls, st);
   if constexpr (sizeof(T) == 2) {
     if (K % 64 == 0) {
       // Direct-to-LDS pipelines, 8 waves per workgroup. Shapes with at least
@@ -924,6 +925,103 @@ bpt_status check_weights(const Plan& p, const bpt_layer_weights* w) {
   return BPT_OK;
 }
 
+// ================================================================= LM head
+// Blockwise LM head with cross-entropy: chunks of chunk_rows rows, whose
+// logits (z W) exist only inside the GEMM's epilogue in the forward and as a
+// chunk x V dlogit buffer in the backward.
+struct LmPlan {
+  int dtype;
+  int64_t n, h, V, c, nb;
+  size_t esz;
+};
+
+bpt_status make_lm_plan(const bpt_lm_head_desc* d, LmPlan& p) {
+  if (!d) return fail(BPT_EINVAL, "desc is NULL");
+  if (d->abi_version != BPT_ABI_VERSION) return fail(BPT_EINVAL, "abi_version mismatch");
+  if (d->dtype != BPT_F32 && d->dtype != BPT_BF16) return fail(BPT_EINVAL, "dtype");
+  if (d->rows < 1 || d->rows > (int64_t(1) << 30)) return fail(BPT_EINVAL, "rows");
+  if (d->hidden < 64 || d->hidden % 64 != 0 || d->hidden > 65536)
+    return fail(BPT_EINVAL, "hidden must be a positive multiple of 64 (<= 65536)");
+  if (d->vocab < 64 || d->vocab % 64 != 0 || d->vocab > (int64_t(1) << 24))
+    return fail(BPT_EINVAL, "vocab must be a positive multiple of 64 (<= 2^24)");
+  if (d->chunk_rows < 64 || d->chunk_rows % 64 != 0)
+    return fail(BPT_EINVAL, "chunk_rows must be a positive multiple of 64");
+  p.dtype = d->dtype; p.n = d->rows; p.h = d->hidden; p.V = d->vocab;
+  p.c = std::min<int64_t>(d->chunk_rows, (d->rows + 63) / 64 * 64);
+  if (p.c * p.V >= (int64_t(1) << 31) || p.c * p.h >= (int64_t(1) << 31))
+    return fail(BPT_EUNSUPPORTED, "chunk_rows x vocab (or x hidden) must stay below 2^31");
+  p.nb = p.V / 32;
+  p.esz = d->dtype == BPT_BF16 ? 2 : 4;
+  return BPT_OK;
+}
+
+struct LmWs {
+  float2* part; float* tlogit; void* dl;
+};
+
+LmWs carve_lm(Carver& c, const LmPlan& p, bool backward) {
+  LmWs w{};
+  if (!backward) {
+    w.part = c.take<float2>(p.c * p.nb);
+    w.tlogit = c.take<float>(p.c);
+  } else {
+    w.dl = c.take<char>(p.c * p.V * p.esz);
+  }
+  return w;
+}
+
+size_t lm_ws_bytes(const LmPlan& p, bool backward) {
+  Carver c(nullptr);
+  carve_lm(c, p, backward);
+  return c.off;
+}
+
+template <typename T>
+bpt_status lm_forward_impl(const LmPlan& p, const T* z, const T* w, const int* tg, float* loss,
+                           float* lse2, void* ws, hipStream_t st) {
+  Carver c(ws);
+  LmWs wk = carve_lm(c, p, false);
+  for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
+    const int64_t rows = std::min(p.c, p.n - r0);
+    EpiCEStats e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V};
+    BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, e, "lm logits",
+                                  nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+    hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       wk.part, p.nb, wk.tlogit, tg + r0, (int)rows, (int)p.V, lse2 + r0,
+                       loss + r0);
+    BPT_TRY(check_launch("ce combine"));
+  }
+  return BPT_OK;
+}
+
+template <typename T>
+bpt_status lm_backward_impl(const LmPlan& p, const T* z, const T* w, const int* tg,
+                            const float* lse2, const float* dloss, T* dz, float* dw,
+                            int accumulate, void* ws, hipStream_t st) {
+  Carver c(ws);
+  LmWs wk = carve_lm(c, p, true);
+  T* dl = (T*)wk.dl;
+  if (dw && !accumulate) BPT_TRY(fill(st, dw, p.h * p.V, 0.f));
+  for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
+    const int64_t rows = std::min(p.c, p.n - r0);
+    EpiCEGrad<T> eg{dl, p.V, lse2 + r0, tg + r0, dloss + r0, (int)p.V};
+    BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, eg,
+                                  "lm logits (re) -> dlogits", nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    if (dz) {
+      EpiOut<T, T> ez{dz + r0 * p.h, p.h, nullptr, 1.f, 0};
+      BPT_TRY((gemm<T, true, true>(st, dl, p.V, w, p.V, rows, p.h, p.V, ez, "lm dz", nullptr, 0,
+                                   BPT_KERNEL_LM_HEAD)));
+    }
+    if (dw) {
+      EpiOut<T, float> ew{dw, p.V, nullptr, 1.f, 1};
+      BPT_TRY((gemm<T, false, false>(st, z + r0 * p.h, p.h, dl, p.V, p.h, p.V, rows, ew, "lm dW",
+                                     nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    }
+  }
+  return BPT_OK;
+}
+
 }  // namespace
 
 // ================================================================= C ABI
@@ -1015,6 +1113,69 @@ bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x, const b
                                st);
   return backward_impl<float>(p, (const float*)x, w, saved, (const float*)dy, (float*)dx, grads, ws,
                               st);
+}
+
+bpt_status bpt_lm_head_validate(const bpt_lm_head_desc* desc) {
+  LmPlan p;
+  return make_lm_plan(desc, p);
+}
+
+size_t bpt_lm_head_saved_size(const bpt_lm_head_desc* desc) {
+  LmPlan p;
+  if (make_lm_plan(desc, p) != BPT_OK) return 0;
+  return (size_t)p.n * 4;
+}
+
+size_t bpt_lm_head_workspace_size(const bpt_lm_head_desc* desc, int32_t backward) {
+  LmPlan p;
+  if (make_lm_plan(desc, p) != BPT_OK) return 0;
+  return lm_ws_bytes(p, backward != 0);
+}
+
+bpt_status bpt_lm_head_forward(const bpt_lm_head_desc* desc, const void* z, const void* w_head,
+                               const int32_t* targets, float* loss, void* saved, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  LmPlan p;
+  BPT_TRY(make_lm_plan(desc, p));
+  if (!z || !w_head || !targets || !loss || !saved || !ws)
+    return fail(BPT_EINVAL, "z, w_head, targets, loss, saved and ws must be non-NULL");
+  if (!aligned16(z) || !aligned16(w_head) || ((uintptr_t)targets & 3) || ((uintptr_t)loss & 3) ||
+      ((uintptr_t)saved & 3) || ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "z, w_head 16-byte, targets/loss/saved 4-byte, ws 256-byte aligned");
+  if (ws_bytes < lm_ws_bytes(p, false)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return lm_forward_impl<bf16>(p, (const bf16*)z, (const bf16*)w_head, targets, loss,
+                                 (float*)saved, ws, st);
+  return lm_forward_impl<float>(p, (const float*)z, (const float*)w_head, targets, loss,
+                                (float*)saved, ws, st);
+}
+
+bpt_status bpt_lm_head_backward(const bpt_lm_head_desc* desc, const void* z, const void* w_head,
+                                const int32_t* targets, const void* saved, const float* dloss,
+                                void* dz, float* dw_head, int32_t accumulate, void* ws,
+                                size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  LmPlan p;
+  BPT_TRY(make_lm_plan(desc, p));
+  if (!z || !w_head || !targets || !saved || !dloss || !ws)
+    return fail(BPT_EINVAL, "z, w_head, targets, saved, dloss and ws must be non-NULL");
+  if (!dz && !dw_head) return fail(BPT_EINVAL, "dz and dw_head are both NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(BPT_EINVAL, "accumulate must be 0 or 1");
+  if (!aligned16(z) || !aligned16(w_head) || (dz && !aligned16(dz)) || ((uintptr_t)targets & 3) ||
+      ((uintptr_t)saved & 3) || ((uintptr_t)dloss & 3) || ((uintptr_t)dw_head & 3) ||
+      ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "z, w_head, dz 16-byte, targets/saved/dloss/dw_head 4-byte, ws 256-byte aligned");
+  if (ws_bytes < lm_ws_bytes(p, true)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return lm_backward_impl<bf16>(p, (const bf16*)z, (const bf16*)w_head, targets,
+                                  (const float*)saved, dloss, (bf16*)dz, dw_head, accumulate, ws,
+                                  st);
+  return lm_backward_impl<float>(p, (const float*)z, (const float*)w_head, targets,
+                                 (const float*)saved, dloss, (float*)dz, dw_head, accumulate, ws,
+                                 st);
 }
 
 const char* bpt_status_string(bpt_status s) {

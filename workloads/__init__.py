@@ -258,3 +258,68 @@ def scaled(t: Tensor, factor: float, cols=slice(None)) -> Tensor:
     vals = t.f32.copy()
     vals[..., cols] *= np.float32(factor)
     return _make(vals, t.dtype)
+
+
+
+# ----------------------------------------------------------------- LM head with cross-entropy
+@dataclasses.dataclass(frozen=True)
+class LmHeadShape:
+    """The output layer with cross-entropy over rows = batch x sequence
+    positions. The vocabulary is padded to a multiple of 64 (the pages' worked
+    example has V = 50257; 50304 = 64 x 786)."""
+    name: str
+    wid: int
+    dtype: str
+    rows: int
+    hidden: int
+    vocab: int
+    chunk_rows: int
+    ignore_every: int = 0      # every n-th row's target is -1 (ignored); 0: none
+
+    def replace(self, **kw) -> "LmHeadShape":
+        return dataclasses.replace(self, **kw)
+
+
+LM_TENSOR_IDS = {"z": 20, "w_head": 21, "targets": 22, "dloss": 23}
+
+LM_HEADS: Dict[str, LmHeadShape] = {
+    # the GPT-1B-shaped model's head over the benchmarked s = 131072 tokens
+    "lmhead-gpt1b-s128k": LmHeadShape("lmhead-gpt1b-s128k", 30, "bf16", 131072, 2048, 50304,
+                                      8192),
+    # reduced shapes: three chunks, the last one ragged, some ignored rows
+    "lmhead-small-bf16": LmHeadShape("lmhead-small-bf16", 31, "bf16", 1000, 256, 1024, 384,
+                                     ignore_every=7),
+    "lmhead-small-f32": LmHeadShape("lmhead-small-f32", 32, "f32", 1000, 256, 1024, 384,
+                                    ignore_every=7),
+}
+
+
+def make_z(sh: LmHeadShape) -> Tensor:
+    """Final hidden states ~ N(0, 1) (the normalised input of the head)."""
+    return _make(_normal(1000 * sh.wid + LM_TENSOR_IDS["z"], (sh.rows, sh.hidden), 1.0), sh.dtype)
+
+
+def make_w_head(sh: LmHeadShape) -> Tensor:
+    """[hidden, vocab] ~ N(0, 1/hidden)."""
+    return _make(_normal(1000 * sh.wid + LM_TENSOR_IDS["w_head"], (sh.hidden, sh.vocab),
+                         sh.hidden ** -0.5), sh.dtype)
+
+
+def make_targets(sh: LmHeadShape) -> np.ndarray:
+    """int32 targets uniform in [0, vocab); every ignore_every-th row -1."""
+    rng = np.random.default_rng(1000 * sh.wid + LM_TENSOR_IDS["targets"])
+    t = rng.integers(0, sh.vocab, size=sh.rows).astype(np.int32)
+    if sh.ignore_every:
+        t[::sh.ignore_every] = -1
+    return t
+
+
+def make_dloss(sh: LmHeadShape, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp32 cotangent of the per-row losses ~ N(0, 1); with ``rows`` only
+    those rows are non-zero."""
+    g = _normal(1000 * sh.wid + LM_TENSOR_IDS["dloss"], (sh.rows,), 1.0)
+    if rows is not None:
+        mask = np.zeros(sh.rows, bool)
+        mask[np.asarray(rows)] = True
+        g[~mask] = 0.0
+    return g
