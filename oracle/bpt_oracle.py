@@ -57,7 +57,7 @@ from typing import Dict, Optional
 import numpy as np
 from scipy.special import erf
 
-__all__ = ["Spec", "spec_of", "layer", "norm_forward", "norm_backward", "rope_rotate",
+__all__ = ["Spec", "spec_of", "layer", "stack", "norm_forward", "norm_backward", "rope_rotate",
            "attention_probs"]
 
 
@@ -336,3 +336,24 @@ def layer(x, w: Dict[str, np.ndarray], sp: Spec, dy=None, rows=None):
         res["dx"] = np.stack(dxs)
         res["grads"] = grads
     return res
+
+
+def stack(x, ws, sp: Spec, dy=None):
+    """L layers applied in sequence, y = layer_L(... layer_1(x)), each with its
+    own weights ws[l] ("Training memory", §3: the model is L such layers; the
+    checkpointing schedule changes what is kept, never the values). The
+    backward runs the layers in reverse, each layer's dx being the cotangent
+    of the layer below. Returns {"y"} and, with dy, "dx" and "grads" (a list
+    of per-layer gradient dicts)."""
+    hs = [np.asarray(x, dtype=np.float64)]
+    for w in ws:
+        hs.append(layer(hs[-1], w, sp)["y"])
+    if dy is None:
+        return {"y": hs[-1]}
+    g = np.asarray(dy, dtype=np.float64)
+    grads = [None] * len(ws)
+    for li in range(len(ws) - 1, -1, -1):
+        out = layer(hs[li], ws[li], sp, dy=g)
+        grads[li] = out["grads"]
+        g = out["dx"]
+    return {"y": hs[-1], "dx": g, "grads": grads}

@@ -358,3 +358,38 @@ def test_row_subset_matches_dense(variant, row_group, monkeypatch):
     assert np.max(np.abs(sub["dx"] - dense["dx"])) < 1e-12
     for name in dense["grads"]:
         assert np.max(np.abs(sub["grads"][name] - dense["grads"][name])) < 1e-12, name
+
+
+def test_stack_central_differences():
+    """A stack of two layers (own weights each): central differences of
+    <y, dy> for the input and every parameter element of both layers."""
+    sh = _shape(norm="layernorm", ffn="gelu", bias=True, s=6, h=8, f=12)
+    ws = [_weights(sh, seed_shift=3), _weights(sh, seed_shift=4)]
+    x, dy = _inputs(sh)
+    sp = orc.spec_of(sh)
+    out = orc.stack(x, ws, sp, dy=dy)
+    eps = 1e-6
+
+    def obj():
+        return float((orc.stack(x, ws, sp)["y"] * dy).sum())
+
+    def fd(arr):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            orig = arr[idx]
+            arr[idx] = orig + eps
+            fp = obj()
+            arr[idx] = orig - eps
+            fm = obj()
+            arr[idx] = orig
+            num[idx] = (fp - fm) / (2 * eps)
+        return num
+
+    assert _rel(out["dx"], fd(x)) < 1e-6
+    for li in range(2):
+        for name in ("w_qkv", "w_o", "w_1", "w_2", "n1_g", "n2_b", "b_qkv"):
+            assert _rel(out["grads"][li][name], fd(ws[li][name])) < 1e-6, (li, name)
+    # one layer is the layer itself
+    one = orc.stack(x, ws[:1], sp, dy=dy)
+    ref = orc.layer(x, ws[0], sp, dy=dy)
+    assert np.array_equal(one["y"], ref["y"]) and np.array_equal(one["dx"], ref["dx"])
