@@ -180,6 +180,45 @@ bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x,
 /* Static description of a status code (never NULL). */
 const char* bpt_status_string(bpt_status status);
 
+/* ---- Stack of layers with activation checkpointing ----
+ * "Training memory...", §3 (full checkpointing; checkpoint every k layers, peak
+ * M(k) = (L/k) c + k A): n_layers layers of one shape, each with its own weights, applied in
+ * sequence. With checkpoint_every = k >= 1 the forward keeps only the input of every k-th
+ * layer (c = one activation [b, s, h]); the backward rebuilds one segment of k layers at a time
+ * from its checkpoint (one extra forward per layer), keeping that segment's layer inputs and
+ * saved states (A per layer), then runs its layers' backward in reverse. k = 0 keeps every
+ * layer's input and saved state from the forward (no recompute). Results do not depend on k. */
+typedef struct {
+  bpt_layer_desc layer;     /* shape and options of every layer */
+  int64_t n_layers;         /* L >= 1 */
+  int64_t checkpoint_every; /* k in 0..L (see above) */
+} bpt_stack_desc;
+
+bpt_status bpt_stack_validate(const bpt_stack_desc* desc);
+
+/* Bytes kept from the forward for the backward: k >= 1: (ceil(L / k) - 1) activations (the
+ * first segment's checkpoint is x itself); k = 0: L - 1 activations and L layer saved buffers
+ * (each rounded up to 256 bytes). */
+size_t bpt_stack_saved_size(const bpt_stack_desc* desc);
+
+/* Forward: two activations plus (k >= 1) one layer saved buffer plus the layer's forward
+ * workspace. Backward: (k >= 1) k - 1 activations, k layer saved buffers and one activation of
+ * the rebuilt segment, two gradient activations, and the layer's workspace. */
+size_t bpt_stack_workspace_size(const bpt_stack_desc* desc, int32_t backward);
+
+/* x, y: [b, s, h]; w: array of n_layers weight tables (layer 0 first); saved and ws 256-byte
+ * aligned. Otherwise as bpt_layer_forward. */
+bpt_status bpt_stack_forward(const bpt_stack_desc* desc, const void* x,
+                             const bpt_layer_weights* w, void* y, void* saved, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* grads: array of n_layers gradient tables (each with its own accumulate flag). x, w and
+ * saved as given to / written by the forward; dy: cotangent of y; dx written. */
+bpt_status bpt_stack_backward(const bpt_stack_desc* desc, const void* x,
+                              const bpt_layer_weights* w, const void* saved, const void* dy,
+                              void* dx, const bpt_layer_grads* grads, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* ---- Blockwise LM head with cross-entropy loss ----
  * "Blockwise Parallel Transformer for Long Context Large Models", §3.4 (handling of the
  * cross-entropy loss: blockwise evaluation never holds all positions' logits) and "Training

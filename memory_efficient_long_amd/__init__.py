@@ -25,6 +25,9 @@ __all__ = [
     "LmHeadConfig", "BptLmHeadDesc", "bpt_lm_head_validate", "bpt_lm_head_saved_size",
     "bpt_lm_head_workspace_size", "bpt_lm_head_forward", "bpt_lm_head_backward",
     "lm_head_forward", "lm_head_backward", "check_lm_head_args",
+    "StackConfig", "BptStackDesc", "bpt_stack_validate", "bpt_stack_saved_size",
+    "bpt_stack_workspace_size", "bpt_stack_forward", "bpt_stack_backward", "stack_forward",
+    "stack_backward",
 ]
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +63,11 @@ class BptLayerWeights(ctypes.Structure):
 class BptLayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES] + [
         ("accumulate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class BptStackDesc(ctypes.Structure):
+    _fields_ = [("layer", BptLayerDesc), ("n_layers", ctypes.c_int64),
+                ("checkpoint_every", ctypes.c_int64)]
 
 
 class BptLmHeadDesc(ctypes.Structure):
@@ -112,6 +120,21 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bpt_layer_forward_noalloc.restype = ctypes.c_int
     lib.bpt_layer_noalloc_scratch_bytes.argtypes = []
     lib.bpt_layer_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    SP = P(BptStackDesc)
+    lib.bpt_stack_validate.argtypes = [SP]
+    lib.bpt_stack_validate.restype = ctypes.c_int
+    lib.bpt_stack_saved_size.argtypes = [SP]
+    lib.bpt_stack_saved_size.restype = ctypes.c_size_t
+    lib.bpt_stack_workspace_size.argtypes = [SP, ctypes.c_int32]
+    lib.bpt_stack_workspace_size.restype = ctypes.c_size_t
+    lib.bpt_stack_forward.argtypes = [SP, ctypes.c_void_p, P(BptLayerWeights), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]
+    lib.bpt_stack_forward.restype = ctypes.c_int
+    lib.bpt_stack_backward.argtypes = [SP, ctypes.c_void_p, P(BptLayerWeights), ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, P(BptLayerGrads),
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.bpt_stack_backward.restype = ctypes.c_int
     LP = P(BptLmHeadDesc)
     lib.bpt_lm_head_validate.argtypes = [LP]
     lib.bpt_lm_head_validate.restype = ctypes.c_int
@@ -546,3 +569,126 @@ def lm_head_backward(cfg: LmHeadConfig, z, w_head, targets, saved, dloss, dz=Non
     if st:
         raise BptError(st, "bpt_lm_head_backward")
     return dz, dw_head
+
+
+# ----------------------------------------------------------------- stack of layers
+@dataclasses.dataclass(frozen=True)
+class StackConfig:
+    """n_layers layers of one shape with checkpointing every k layers
+    (mirrors bpt_stack_desc; k = 0 keeps every layer's saved state)."""
+    layer: LayerConfig
+    n_layers: int
+    checkpoint_every: int = 1
+
+    def desc(self) -> BptStackDesc:
+        return BptStackDesc(layer=self.layer.desc(), n_layers=self.n_layers,
+                            checkpoint_every=self.checkpoint_every)
+
+
+def _stack_desc(d) -> BptStackDesc:
+    return d.desc() if isinstance(d, StackConfig) else d
+
+
+def bpt_stack_validate(desc) -> int:
+    return load_library().bpt_stack_validate(ctypes.byref(_stack_desc(desc)))
+
+
+def bpt_stack_saved_size(desc) -> int:
+    return load_library().bpt_stack_saved_size(ctypes.byref(_stack_desc(desc)))
+
+
+def bpt_stack_workspace_size(desc, backward: bool) -> int:
+    return load_library().bpt_stack_workspace_size(ctypes.byref(_stack_desc(desc)), int(backward))
+
+
+def _check_stack(d, x, weights_list, saved, workspace, backward):
+    if len(weights_list) != d.n_layers:
+        raise ValueError(f"{len(weights_list)} weight tables for {d.n_layers} layers")
+    n = d.layer.batch * d.layer.seq_len * d.layer.hidden
+    dt = _TORCH_DTYPE_NAMES.get(d.layer.dtype)
+    if dt is None:
+        raise ValueError("descriptor dtype")
+    _check_tensor(x, "x", None, dtype=dt, numel=n)
+    for wdict in weights_list:
+        _check_weights(d.layer, wdict, x.device)
+    if bpt_stack_saved_size(d):
+        _check_tensor(saved, "saved", x.device, min_bytes=bpt_stack_saved_size(d))
+    _check_tensor(workspace, "workspace", x.device,
+                  min_bytes=bpt_stack_workspace_size(d, backward))
+    return n, dt
+
+
+def bpt_stack_forward(desc, x, weights_list, y, saved, workspace, stream=None) -> int:
+    """Raw call: weights_list holds one weight dict per layer (checked first)."""
+    d = _stack_desc(desc)
+    n, dt = _check_stack(d, x, weights_list, saved, workspace, False)
+    _check_tensor(y, "y", x.device, dtype=dt, numel=n)
+    ws_arr = (BptLayerWeights * d.n_layers)(*[_weights_struct(w) for w in weights_list])
+    return load_library().bpt_stack_forward(
+        ctypes.byref(d), _ptr(x), ws_arr, _ptr(y), _ptr(saved), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def bpt_stack_backward(desc, x, weights_list, saved, dy, dx, grads_list, workspace,
+                       accumulate=False, stream=None) -> int:
+    """Raw call: grads_list holds one dict of fp32 gradients per layer."""
+    d = _stack_desc(desc)
+    n, dt = _check_stack(d, x, weights_list, saved, workspace, True)
+    _check_tensor(dy, "dy", x.device, dtype=dt, numel=n)
+    _check_tensor(dx, "dx", x.device, dtype=dt, numel=n)
+    if len(grads_list) != d.n_layers:
+        raise ValueError(f"{len(grads_list)} gradient tables for {d.n_layers} layers")
+    shapes = weight_shapes_of(d.layer)
+    for grads in grads_list:
+        for g, tns in grads.items():
+            if tns is None:
+                continue
+            if g not in GRAD_NAMES or g[1:] not in shapes:
+                raise ValueError(f"{g} is not a gradient of this layer")
+            _check_tensor(tns, g, x.device, dtype="float32", shape=shapes[g[1:]])
+    g_arr = (BptLayerGrads * d.n_layers)(*[
+        BptLayerGrads(**{k: _ptr(gr.get(k)) for k in GRAD_NAMES}, accumulate=int(accumulate),
+                      reserved=0) for gr in grads_list])
+    ws_arr = (BptLayerWeights * d.n_layers)(*[_weights_struct(w) for w in weights_list])
+    return load_library().bpt_stack_backward(
+        ctypes.byref(d), _ptr(x), ws_arr, _ptr(saved), _ptr(dy), _ptr(dx), g_arr, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def _alloc_aligned_bytes(n: int, device):
+    """A byte tensor whose data pointer is 256-byte aligned (torch's caching
+    allocator returns such blocks)."""
+    t = _alloc_bytes(n, device)
+    if t.data_ptr() % 256:
+        raise RuntimeError("allocation not 256-byte aligned")
+    return t
+
+
+def stack_forward(cfg: StackConfig, x, weights_list, stream=None):
+    """y, saved = stack_forward(cfg, x, weights_list): allocates what it needs."""
+    import torch
+    d = cfg.desc()
+    st = bpt_stack_validate(d)
+    if st:
+        raise BptError(st, "bpt_stack_validate")
+    y = torch.empty_like(x)
+    saved = _alloc_aligned_bytes(bpt_stack_saved_size(d), x.device)
+    ws = _alloc_aligned_bytes(bpt_stack_workspace_size(d, False), x.device)
+    st = bpt_stack_forward(d, x, weights_list, y, saved, ws, stream)
+    if st:
+        raise BptError(st, "bpt_stack_forward")
+    return y, saved
+
+
+def stack_backward(cfg: StackConfig, x, weights_list, saved, dy, stream=None):
+    """dx, grads_list = stack_backward(...): fp32 gradients for every layer."""
+    import torch
+    d = cfg.desc()
+    dx = torch.empty_like(x)
+    grads_list = [{k: torch.empty(s, dtype=torch.float32, device=x.device)
+                   for k, s in grad_shapes(cfg.layer, w).items()} for w in weights_list]
+    ws = _alloc_aligned_bytes(bpt_stack_workspace_size(d, True), x.device)
+    st = bpt_stack_backward(d, x, weights_list, saved, dy, dx, grads_list, ws, False, stream)
+    if st:
+        raise BptError(st, "bpt_stack_backward")
+    return dx, grads_list

@@ -925,6 +925,114 @@ bpt_status check_weights(const Plan& p, const bpt_layer_weights* w) {
   return BPT_OK;
 }
 
+// ================================================================= layer stack
+// L layers with checkpointing every k layers ("Training memory...", §3,
+// checkpoint every k layers: the input of every k-th layer is kept; the
+// backward rebuilds one segment of k layers at a time, keeping that segment's
+// layer inputs and saved states, then runs its layers' backward in reverse).
+// k = 0 keeps every layer's input and saved state (no recompute).
+struct StackPlan {
+  Plan lp;
+  int64_t L, k, nck;  // nck: checkpoint slots (k >= 1) or stored inputs (k = 0)
+  size_t act, sv;     // one activation [b, s, h] and one layer saved buffer, 256-aligned
+};
+
+bpt_status make_stack_plan(const bpt_stack_desc* d, StackPlan& sp) {
+  if (!d) return fail(BPT_EINVAL, "desc is NULL");
+  BPT_TRY(make_plan(&d->layer, sp.lp));
+  if (d->n_layers < 1 || d->n_layers > 4096) return fail(BPT_EINVAL, "n_layers must be 1..4096");
+  if (d->checkpoint_every < 0 || d->checkpoint_every > d->n_layers)
+    return fail(BPT_EINVAL, "checkpoint_every must be 0..n_layers");
+  sp.L = d->n_layers;
+  sp.k = d->checkpoint_every;
+  sp.nck = sp.k ? (sp.L + sp.k - 1) / sp.k - 1 : sp.L - 1;
+  sp.act = align_up((size_t)(sp.lp.b * sp.lp.s * sp.lp.h) * sp.lp.esz, 256);
+  sp.sv = align_up(saved_bytes(sp.lp), 256);
+  return BPT_OK;
+}
+
+size_t stack_saved_bytes(const StackPlan& sp) {
+  return (size_t)sp.nck * sp.act + (sp.k ? 0 : (size_t)sp.L * sp.sv);
+}
+
+// Forward workspace: two ping-pong activations, one transient saved buffer
+// (k >= 1) and the layer's forward workspace.
+size_t stack_fwd_ws_bytes(const StackPlan& sp) {
+  return 2 * sp.act + (sp.k ? sp.sv : 0) + fwd_ws_bytes(sp.lp);
+}
+
+// Backward workspace: the rebuilt segment (k - 1 layer inputs, k saved
+// buffers, one scratch output) for k >= 1, two gradient ping-pong buffers and
+// the layer workspace.
+size_t stack_bwd_ws_bytes(const StackPlan& sp) {
+  const size_t lw = std::max(fwd_ws_bytes(sp.lp), bwd_ws_bytes(sp.lp));
+  const size_t seg = sp.k ? (size_t)(sp.k - 1) * sp.act + (size_t)sp.k * sp.sv + sp.act : 0;
+  return seg + 2 * sp.act + (sp.k ? lw : bwd_ws_bytes(sp.lp));
+}
+
+template <typename T>
+bpt_status stack_forward_impl(const StackPlan& sp, const T* x, const bpt_layer_weights* w, T* y,
+                              char* saved, char* ws, hipStream_t st) {
+  char* pp[2] = {ws, ws + sp.act};
+  char* tsaved = ws + 2 * sp.act;
+  char* lws = tsaved + (sp.k ? sp.sv : 0);
+  const T* cur = x;
+  for (int64_t l = 0; l < sp.L; ++l) {
+    T* out;
+    if (l == sp.L - 1) out = y;
+    else if (sp.k == 0) out = (T*)(saved + (size_t)l * sp.act);            // input of layer l + 1
+    else if ((l + 1) % sp.k == 0) out = (T*)(saved + (size_t)((l + 1) / sp.k - 1) * sp.act);
+    else out = (T*)pp[l & 1];
+    void* lsaved = sp.k ? (void*)tsaved : (void*)(saved + (size_t)sp.nck * sp.act + l * sp.sv);
+    BPT_TRY(forward_impl<T>(sp.lp, cur, &w[l], out, lsaved, lws, st));
+    cur = out;
+  }
+  return BPT_OK;
+}
+
+template <typename T>
+bpt_status stack_backward_impl(const StackPlan& sp, const T* x, const bpt_layer_weights* w,
+                               const char* saved, const T* dy, T* dx, const bpt_layer_grads* gr,
+                               char* ws, hipStream_t st) {
+  const int64_t kk = sp.k ? sp.k : sp.L;
+  char* seg_in = ws;                                        // k - 1 layer inputs
+  char* seg_sv = seg_in + (sp.k ? (size_t)(sp.k - 1) * sp.act : 0);
+  char* scratch = seg_sv + (sp.k ? (size_t)sp.k * sp.sv : 0);
+  char* gb[2] = {scratch + (sp.k ? sp.act : 0), scratch + (sp.k ? sp.act : 0) + sp.act};
+  char* lws = gb[1] + sp.act;
+  const T* g_cur = dy;
+  const int64_t nseg = (sp.L + kk - 1) / kk;
+  std::vector<const T*> in(kk + 1);
+  std::vector<const void*> sv(kk);
+  for (int64_t j = nseg - 1; j >= 0; --j) {
+    const int64_t l0 = j * kk, cnt = std::min(kk, sp.L - l0);
+    if (sp.k) {
+      // Rebuild the segment from its checkpoint: each layer's input and saved state.
+      in[0] = j == 0 ? x : (const T*)(saved + (size_t)(j - 1) * sp.act);
+      for (int64_t i = 0; i < cnt; ++i) {
+        T* out = i < cnt - 1 ? (T*)(seg_in + (size_t)i * sp.act) : (T*)scratch;
+        void* lsv = seg_sv + (size_t)i * sp.sv;
+        BPT_TRY(forward_impl<T>(sp.lp, in[i], &w[l0 + i], out, lsv, lws, st));
+        in[i + 1] = out;
+        sv[i] = lsv;
+      }
+    } else {
+      for (int64_t i = 0; i < cnt; ++i) {
+        const int64_t l = l0 + i;
+        in[i] = l == 0 ? x : (const T*)(saved + (size_t)(l - 1) * sp.act);
+        sv[i] = saved + (size_t)sp.nck * sp.act + (size_t)l * sp.sv;
+      }
+    }
+    for (int64_t i = cnt - 1; i >= 0; --i) {
+      const int64_t l = l0 + i;
+      T* g_out = l == 0 ? dx : (T*)(g_cur == (const T*)gb[0] ? gb[1] : gb[0]);
+      BPT_TRY(backward_impl<T>(sp.lp, in[i], &w[l], sv[i], g_cur, g_out, &gr[l], lws, st));
+      g_cur = g_out;
+    }
+  }
+  return BPT_OK;
+}
+
 // ================================================================= LM head
 // Blockwise LM head with cross-entropy: chunks of chunk_rows rows, whose
 // logits (z W) exist only inside the GEMM's epilogue in the forward and as a
@@ -1113,6 +1221,74 @@ bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x, const b
                                st);
   return backward_impl<float>(p, (const float*)x, w, saved, (const float*)dy, (float*)dx, grads, ws,
                               st);
+}
+
+bpt_status bpt_stack_validate(const bpt_stack_desc* desc) {
+  StackPlan sp;
+  return make_stack_plan(desc, sp);
+}
+
+size_t bpt_stack_saved_size(const bpt_stack_desc* desc) {
+  StackPlan sp;
+  if (make_stack_plan(desc, sp) != BPT_OK) return 0;
+  return stack_saved_bytes(sp);
+}
+
+size_t bpt_stack_workspace_size(const bpt_stack_desc* desc, int32_t backward) {
+  StackPlan sp;
+  if (make_stack_plan(desc, sp) != BPT_OK) return 0;
+  return backward ? stack_bwd_ws_bytes(sp) : stack_fwd_ws_bytes(sp);
+}
+
+bpt_status bpt_stack_forward(const bpt_stack_desc* desc, const void* x,
+                             const bpt_layer_weights* w, void* y, void* saved, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  StackPlan sp;
+  BPT_TRY(make_stack_plan(desc, sp));
+  if (!w) return fail(BPT_EINVAL, "weights is NULL");
+  for (int64_t l = 0; l < sp.L; ++l) BPT_TRY(check_weights(sp.lp, &w[l]));
+  if (!x || !y || !ws || (stack_saved_bytes(sp) && !saved))
+    return fail(BPT_EINVAL, "x, y, ws (and saved unless empty) must be non-NULL");
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)saved & 255) || ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "x, y 16-byte and saved, ws 256-byte aligned");
+  if (ws_bytes < stack_fwd_ws_bytes(sp)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (sp.lp.dtype == BPT_BF16)
+    return stack_forward_impl<bf16>(sp, (const bf16*)x, w, (bf16*)y, (char*)saved, (char*)ws, st);
+  return stack_forward_impl<float>(sp, (const float*)x, w, (float*)y, (char*)saved, (char*)ws, st);
+}
+
+bpt_status bpt_stack_backward(const bpt_stack_desc* desc, const void* x,
+                              const bpt_layer_weights* w, const void* saved, const void* dy,
+                              void* dx, const bpt_layer_grads* grads, void* ws, size_t ws_bytes,
+                              void* stream) {
+  g_last_error.clear();
+  StackPlan sp;
+  BPT_TRY(make_stack_plan(desc, sp));
+  if (!w || !grads) return fail(BPT_EINVAL, "weights and grads must be non-NULL");
+  for (int64_t l = 0; l < sp.L; ++l) {
+    BPT_TRY(check_weights(sp.lp, &w[l]));
+    const bpt_layer_grads& g = grads[l];
+    if (g.accumulate != 0 && g.accumulate != 1)
+      return fail(BPT_EINVAL, "grads[l].accumulate must be 0 or 1");
+    const float* gp[13] = {g.dw_qkv, g.db_qkv, g.dw_o, g.db_o, g.dw_1, g.db_1, g.dw_2,
+                           g.db_2, g.dw_3, g.dn1_g, g.dn1_b, g.dn2_g, g.dn2_b};
+    for (const float* q : gp)
+      if (q && ((uintptr_t)q & 3)) return fail(BPT_EINVAL, "gradient buffer misaligned");
+  }
+  if (!x || !dy || !dx || !ws || (stack_saved_bytes(sp) && !saved))
+    return fail(BPT_EINVAL, "x, dy, dx, ws (and saved unless empty) must be non-NULL");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || ((uintptr_t)saved & 255) ||
+      ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL, "x, dy, dx 16-byte and saved, ws 256-byte aligned");
+  if (ws_bytes < stack_bwd_ws_bytes(sp)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (sp.lp.dtype == BPT_BF16)
+    return stack_backward_impl<bf16>(sp, (const bf16*)x, w, (const char*)saved, (const bf16*)dy,
+                                     (bf16*)dx, grads, (char*)ws, st);
+  return stack_backward_impl<float>(sp, (const float*)x, w, (const char*)saved, (const float*)dy,
+                                    (float*)dx, grads, (char*)ws, st);
 }
 
 bpt_status bpt_lm_head_validate(const bpt_lm_head_desc* desc) {

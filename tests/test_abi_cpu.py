@@ -344,3 +344,47 @@ def test_noalloc_forward_refuses_layers_beyond_its_scratch():
     # argument errors come first, as in bpt_layer_forward
     assert lib.bpt_layer_forward_noalloc(ctypes.byref(d), None, ctypes.byref(w), fake, fake,
                                          None) == 1
+
+
+@pytest.mark.parametrize("L,k", [(1, 1), (3, 0), (3, 1), (3, 2), (3, 3), (8, 2), (8, 3)])
+def test_stack_memory_follows_checkpoint_every_k(L, k):
+    """Saved bytes: (ceil(L / k) - 1) checkpoints of one activation c for
+    k >= 1 (the first segment's is x), or L - 1 activations and L saved
+    states for k = 0. Backward peak (saved + workspace) for k >= 1:
+    (ceil(L / k) - 1) c + k rebuilt layers (input + saved state) + scratch and
+    gradient activations + the layer workspace: the (L/k) c + k A of
+    "Training memory", §3 (checkpoint every k layers)."""
+    sh = wl.WORKLOADS["gpt1b-s8k"]
+    layer = bpt.LayerConfig.from_shape(sh)
+    d = bpt.StackConfig(layer, L, k).desc()
+    assert bpt.bpt_stack_validate(d) == 0
+    ld = layer.desc()
+    c = sh.seq_len * sh.hidden * 2
+    sv = -(-bpt.bpt_layer_saved_size(ld) // 256) * 256
+    lw = max(bpt.bpt_layer_workspace_size(ld, False), bpt.bpt_layer_workspace_size(ld, True))
+    saved = bpt.bpt_stack_saved_size(d)
+    wsb = bpt.bpt_stack_workspace_size(d, True)
+    if k == 0:
+        assert saved == (L - 1) * c + L * sv
+        assert wsb == 2 * c + bpt.bpt_layer_workspace_size(ld, True)
+    else:
+        n_ck = -(-L // k) - 1
+        assert saved == n_ck * c
+        assert saved + wsb == (n_ck + (k - 1) + 1 + 2) * c + k * sv + lw
+    assert bpt.bpt_stack_workspace_size(d, False) == 2 * c + (sv if k else 0) + \
+        bpt.bpt_layer_workspace_size(ld, False)
+
+
+def test_stack_descriptor_rules():
+    layer = bpt.LayerConfig.from_shape(wl.WORKLOADS["gpt1b-s8k"])
+    assert bpt.bpt_stack_validate(bpt.StackConfig(layer, 0, 0).desc()) == 1
+    assert bpt.bpt_stack_validate(bpt.StackConfig(layer, 3, 4).desc()) == 1
+    assert bpt.bpt_stack_validate(bpt.StackConfig(layer, 3, -1).desc()) == 1
+    bad = dataclasses_replace(layer, q_block=1000)
+    assert bpt.bpt_stack_validate(bpt.StackConfig(bad, 3, 1).desc()) == 1
+    assert bpt.bpt_stack_saved_size(bpt.StackConfig(layer, 3, 4).desc()) == 0
+
+
+def dataclasses_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)

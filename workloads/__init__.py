@@ -86,6 +86,14 @@ WORKLOADS: Dict[str, LayerShape] = {
                                "rmsnorm", "swiglu", False, True, None, 1024, 2048, 64),
 }
 
+# The small-hidden shape of the pages' reinforcement-learning experiment: an
+# Agentic-Transformer-style GPT of 3 layers, embedding 128, one attention head,
+# over 32 trajectories x 1000 steps x 4 tokens = 128000 positions (one
+# trajectory per query block). Run as a stack of 3 layers.
+RL_SMALL_H = LayerShape("rl-small-h-s128k", 6, "bf16", 1, 128000, 128, 1, 1, 128, 512,
+                        "layernorm", "gelu", True, True, None, 4000, 4000, 1)
+RL_SMALL_H_LAYERS = 3
+
 # Reduced shapes that keep each workload's structure (dtype, norm, FFN kind,
 # GQA grouping, RoPE, head chunking) at sizes the float64 oracle finishes in
 # seconds; sequence lengths are chosen so the last attention and GEMM tiles are
@@ -323,3 +331,11 @@ def make_dloss(sh: LmHeadShape, rows: Optional[np.ndarray] = None) -> np.ndarray
         mask[np.asarray(rows)] = True
         g[~mask] = 0.0
     return g
+
+
+def make_stack_weights(sh: LayerShape, n_layers: int, bias_std: float = 0.0,
+                       norm_std: float = 0.0):
+    """One weight set per layer of a stack; layer l draws from seed family
+    wid + 1000 (l + 1)."""
+    return [make_weights(sh.replace(wid=sh.wid + 1000 * (li + 1)), bias_std, norm_std)
+            for li in range(n_layers)]
