@@ -170,8 +170,137 @@ def memory_sweep() -> int:
     for u in (4, 8, 16, 32):
         print(f"[memory] llama8b head_chunk={u}", file=sys.stderr, flush=True)
         chunks.append(_peak_activation_bytes(llama.replace(head_chunk=u)))
+    stack = []
+    st_shape = base.replace(seq_len=16384)
+    for k in (0, 1, 2, 4, 8):
+        print(f"[memory] gpt1b stack L=8 k={k}", file=sys.stderr, flush=True)
+        stack.append(_stack_peak_bytes(st_shape, 8, k))
     print(json.dumps({"memory_sweep": {"gpt1b": pts, "affine_fit": fit,
-                                       "llama8b_head_chunk": chunks}}), flush=True)
+                                       "llama8b_head_chunk": chunks,
+                                       "gpt1b_s16k_stack_L8": stack}}), flush=True)
+    return 0
+
+
+def _stack_peak_bytes(sh, L, k) -> dict:
+    """Peak of a stack forward + backward: the library's saved + workspace
+    bytes, the checkpoint-every-k prediction (L/k) c + k A with c one
+    activation and A one layer's rebuilt input and saved state, and torch's
+    peak allocation above the inputs, weights and gradients."""
+    import torch
+    import memory_efficient_long_amd as bpt
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    cfg = bpt.StackConfig(bpt.LayerConfig.from_shape(sh), L, k)
+    d = cfg.desc()
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(sh.batch, sh.seq_len, sh.hidden, device=dev, generator=gen).to(torch.bfloat16)
+    ws = [{n: (torch.randn(s, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+           for n, s in wl.weight_shapes(sh).items()} for _ in range(L)]
+    dy = torch.randn_like(x)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    y, saved = bpt.stack_forward(cfg, x, ws)
+    dx, grads = bpt.stack_backward(cfg, x, ws, saved, dy)
+    torch.cuda.synchronize()
+    gbytes = sum(v.numel() * 4 for g in grads for v in g.values())
+    peak = torch.cuda.max_memory_allocated(dev) - base - gbytes - 2 * x.numel() * 2
+    lib = bpt.bpt_stack_saved_size(d) + max(bpt.bpt_stack_workspace_size(d, False),
+                                            bpt.bpt_stack_workspace_size(d, True))
+    c = x.numel() * 2
+    A = c + bpt.bpt_layer_saved_size(cfg.layer.desc())
+    pred = (L / k * c + k * A) if k else None
+    del x, ws, dy, y, saved, dx, grads
+    torch.cuda.empty_cache()
+    return {"k": k, "library_bytes": lib, "torch_peak_bytes": int(peak),
+            "pages_M_k_bytes": pred}
+
+
+def bench_stack(args, sh, L, k) -> int:
+    """One step = forward + backward of a stack of L layers (own weights
+    each) with checkpointing every k layers, inputs resident in HBM."""
+    import numpy as np
+    import torch
+    import memory_efficient_long_amd as bpt
+    import workloads as wl
+    dev = torch.device("cuda:0")
+
+    def to_dev(t):
+        if t.dtype == "bf16":
+            return torch.from_numpy(t.storage.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(t.storage).to(dev)
+
+    cfg = bpt.StackConfig(bpt.LayerConfig.from_shape(sh), L, k)
+    d = cfg.desc()
+    x, dy = to_dev(wl.make_x(sh)), to_dev(wl.make_dy(sh))
+    ws = [{n: to_dev(v) for n, v in w.items()} for w in wl.make_stack_weights(sh, L)]
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    saved = torch.empty(max(bpt.bpt_stack_saved_size(d), 256), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(bpt.bpt_stack_workspace_size(d, False), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(bpt.bpt_stack_workspace_size(d, True), dtype=torch.uint8, device=dev)
+    grads = [{n: torch.empty(s, dtype=torch.float32, device=dev)
+              for n, s in bpt.grad_shapes(cfg.layer, w).items()} for w in ws]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = bpt.bpt_stack_forward(d, x, ws, y, saved, wsf, stream)
+        st = st or bpt.bpt_stack_backward(d, x, ws, saved, dy, dx, grads, wsb, False, stream)
+        if st:
+            raise bpt.BptError(st, "stack")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    attn = ["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"]
+    bpt.bpt_timing_enable(attn)
+    bpt.bpt_timing_read(reset=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    timing = bpt.bpt_timing_read(reset=True)
+    bpt.bpt_timing_enable([])
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    fl = model_flops(sh)
+    model = L * fl["step"]
+    peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
+    tokens = sh.seq_len * sh.batch
+    # the dominant unit, as for one layer (k >= 1 runs each layer's attention
+    # forward twice per step)
+    unit_ms = {u: sum(timing[c][0] for c in cs) for u, cs in ROOFLINE_UNITS.items()}
+    dom = max(unit_ms, key=unit_ms.get)
+    n_launch = timing[ROOFLINE_UNITS[dom][0]][1]
+    avg_ms = sum(timing[c][0] / max(timing[c][1], 1) for c in ROOFLINE_UNITS[dom])
+    achieved = fl[dom] / (avg_ms * 1e-3) / 1e12 if avg_ms > 0 else 0.0
+    saved_b = bpt.bpt_stack_saved_size(d)
+    peak_b = saved_b + max(wsf.numel(), wsb.numel())
+    out = {
+        "metric": "BPT layer stack fwd+bwd tokens/s (checkpointing every k layers)",
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
+        "data": "synthetic",
+        "config": {"workload": sh.name, "n_layers": L, "checkpoint_every": k,
+                   "seq_len": sh.seq_len, "hidden": sh.hidden, "n_heads": sh.n_heads,
+                   "head_dim": sh.head_dim, "ffn_dim": sh.ffn_dim, "q_block": sh.q_block,
+                   "kv_block": sh.kv_block},
+        "model_tflops": round(model / (ms * 1e-3) / 1e12, 2),
+        "mfma_peak_frac": round(model / (ms * 1e-3) / 1e12 / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": " + ".join(c + "_dma_kernel" for c in ROOFLINE_UNITS[dom]),
+                     "avg_launch_ms": round(avg_ms, 3), "launches_per_step": n_launch / args.steps},
+        "memory": {"saved_bytes_per_token": saved_b / tokens,
+                   "saved_sbh": round(saved_b / (tokens * sh.hidden), 3),
+                   "peak_bytes_per_token": peak_b / tokens,
+                   "peak_sbh": round(peak_b / (tokens * sh.hidden), 3)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -231,7 +360,7 @@ def bench_lm_head(args) -> int:
     model = 6 * n * h * V          # logits, dz and dW products (2nhV each)
     hw = 8 * n * h * V             # + the logits recomputed in the backward
     gm, gn = timing["lm_head"]
-    achieved = model / args.steps / (gm / args.steps * 1e-3) / 1e12 if gm > 0 else 0.0
+    achieved = model / (gm / args.steps * 1e-3) / 1e12 if gm > 0 else 0.0
     peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
     out = {
         "metric": "blockwise LM head + cross-entropy fwd+bwd tokens/s",
@@ -293,6 +422,10 @@ def main() -> int:
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
+    ap.add_argument("--stack", type=int, default=0, metavar="L",
+                    help="time a stack of L layers of the workload's shape instead of one layer")
+    ap.add_argument("--checkpoint-every", type=int, default=1, metavar="K",
+                    help="stack checkpoint interval (0: keep every layer's saved state)")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="only measure peak activation bytes over s (GPT-1B shape) and head chunk "
                          "(Llama-8B shape) and print one JSON line")
@@ -328,6 +461,14 @@ def main() -> int:
         return memory_sweep()
     if args.workload in wl.LM_HEADS:
         return bench_lm_head(args)
+    if args.workload == wl.RL_SMALL_H.name:
+        return bench_stack(args, wl.RL_SMALL_H, args.stack or wl.RL_SMALL_H_LAYERS,
+                           args.checkpoint_every)
+    if args.stack:
+        sh = wl.WORKLOADS[args.workload]
+        if args.head_chunk:
+            sh = sh.replace(head_chunk=args.head_chunk)
+        return bench_stack(args, sh, args.stack, args.checkpoint_every)
     sh = wl.WORKLOADS[args.workload]
     if args.head_chunk:
         sh = sh.replace(head_chunk=args.head_chunk)
