@@ -208,9 +208,10 @@ FwdWs<T> carve_fwd(Carver& c, const Plan& p) {
     w.wc = c.take<T>(p.h * p.chunk_cols);
     w.bc = c.take<T>(p.chunk_cols);
   }
-  w.h1 = c.take<float>(p.s * p.h);  // x + attention output projection, whole sequence
-  // FFN scratch for a group of gq query blocks.
+  // FFN scratch for a group of gq query blocks, with the group's
+  // h1 = x + O W_o + b_o (fp32).
   const int64_t grp = p.gq * p.cq;
+  w.h1 = c.take<float>(grp * p.h);
   w.z = c.take<T>(grp * p.h);
   w.u = c.take<T>(grp * p.f);
   w.gate = p.ffn == BPT_SWIGLU ? c.take<T>(grp * p.f) : nullptr;
@@ -243,9 +244,10 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
     w.wc = c.take<T>(p.h * p.chunk_cols);
     w.bc = c.take<T>(p.chunk_cols);
   }
-  w.h1 = c.take<float>(p.s * p.h);  // recomputed x + O W_o + b_o, whole sequence
-  // FFN activations and gradients for a group of gq query blocks.
+  // FFN activations and gradients for a group of gq query blocks, with the
+  // group's recomputed h1 = x + O W_o + b_o (fp32).
   const int64_t grp = p.gq * p.cq;
+  w.h1 = c.take<float>(grp * p.h);
   w.z = c.take<T>(grp * p.h);
   w.a = c.take<T>(grp * p.f);
   w.u = c.take<T>(grp * p.f);
@@ -661,17 +663,17 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
       BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s));
     }
-    // Output projection + residual for the whole sequence in one GEMM (it is
-    // position-wise; only the FFN needs the per-block scratch).
-    {
-      EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
-      BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection")));
-    }
-    // Norm2 and the FFN, a group of gq consecutive query blocks at a time.
+    // Output projection + residual, Norm2 and the FFN, a group of gq
+    // consecutive query blocks at a time.
     const int64_t grp = p.gq * p.cq;
     for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
       const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
-      const float* h1g = w.h1 + g0 * p.h;
+      const float* h1g = w.h1;
+      {
+        EpiResid<T, T, float> eo{w.h1, p.h, xb + g0 * p.h, p.h, bo};
+        BPT_TRY((gemm<T, true, false>(st, Ob + g0 * HD, HD, wo, p.h, rows, p.h, HD, eo,
+                                      "o projection")));
+      }
       BPT_TRY((norm_fwd<T, float, T>(st, p, h1g, p.h, g2, sh2, w.z, p.h, rows)));
       if (p.ffn == BPT_SWIGLU) {
         EpiOut<T, T> eg{w.gate, p.f, b1, 1.f, 0};
@@ -736,19 +738,20 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     const float* Lb = LSE + bi * p.H * p.s;
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
 
-    // ---- h1 = x + O W_o + b_o recomputed for the whole sequence
-    {
-      EpiResid<T, T, float> eo{w.h1, p.h, xb, p.h, bo};
-      BPT_TRY((gemm<T, true, false>(st, Ob, HD, wo, p.h, p.s, p.h, HD, eo, "o projection (re)")));
-    }
     // ---- FFN and Norm2 backward, a group of gq consecutive query blocks at
-    // a time (the whole FFN chain of the group, then its weight gradients).
+    // a time (h1 = x + O W_o + b_o recomputed for the group, the whole FFN
+    // chain of the group, then its weight gradients).
     int np_db1 = 0, np_n2 = 0;
     const int64_t grp = p.gq * p.cq;
     for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
       const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
       const T* dyg = dyb + g0 * p.h;
-      const float* h1g = w.h1 + g0 * p.h;
+      const float* h1g = w.h1;
+      {
+        EpiResid<T, T, float> eo{w.h1, p.h, xb + g0 * p.h, p.h, bo};
+        BPT_TRY((gemm<T, true, false>(st, Ob + g0 * HD, HD, wo, p.h, rows, p.h, HD, eo,
+                                      "o projection (re)")));
+      }
       BPT_TRY((norm_fwd<T, float, T>(st, p, h1g, p.h, g2, sh2, w.z, p.h, rows)));
       if (swiglu) {
         EpiOut<T, T> eg{w.a, p.f, b1, 1.f, 0};   // w.a holds the gate pre-activation
