@@ -73,13 +73,14 @@ class Spec:
     causal: bool = True
     rope_base: Optional[float] = None
     eps: float = 1e-5
+    window: int = 0                # causal sliding window W (0: none)
 
 
 def spec_of(shape) -> Spec:
     """Spec from any object carrying the layer's shape attributes."""
     return Spec(shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
                 shape.norm, shape.ffn, shape.causal, shape.rope_base,
-                getattr(shape, "norm_eps", 1e-5))
+                getattr(shape, "norm_eps", 1e-5), getattr(shape, "window", 0))
 
 
 # --------------------------------------------------------------------------- norms
@@ -135,15 +136,22 @@ def rope_rotate(t, positions, base, sign=+1.0):
 
 
 # --------------------------------------------------------------------------- attention
-def attention_probs(q_h, k_h, rows, causal):
+def attention_probs(q_h, k_h, rows, causal, window=0):
     """Softmax(q k^T / sqrt(d)) for query rows ``rows`` (positions) against keys
     0..n-1, one explicit score row at a time: shift by the row max, exponentiate,
-    normalise by the row sum."""
+    normalise by the row sum. The positional bias is -inf for keys after the
+    query (causal) and, with a window W, for keys W or more positions before
+    it ("Blockwise Parallel Transformer", §3.4: a bias from the absolute
+    positions of the query and key, -inf where a key is not visible)."""
     d = q_h.shape[-1]
     n = k_h.shape[0]
     scores = (q_h @ k_h.T) / np.sqrt(d)
+    rr = np.asarray(rows)[:, None]
+    jj = np.arange(n)[None, :]
     if causal:
-        scores = np.where(np.asarray(rows)[:, None] >= np.arange(n)[None, :], scores, -np.inf)
+        scores = np.where(rr >= jj, scores, -np.inf)
+    if window:
+        scores = np.where(rr - jj < window, scores, -np.inf)
     m = scores.max(axis=1, keepdims=True)
     e = np.exp(scores - m)
     return e / e.sum(axis=1, keepdims=True)
@@ -222,7 +230,7 @@ def _sequence(x, w, sp: Spec, rows, dy):
     for hq in range(H):
         kv = hq // G
         for sl, nk in _row_groups(rows, n, sp.causal):
-            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal)
+            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal, sp.window)
             attn[sl, hq] = p @ v[:nk, kv]
     attn2 = attn.reshape(r, H * d)
 
@@ -277,7 +285,7 @@ def _sequence(x, w, sp: Spec, rows, dy):
     for hq in range(H):
         kv = hq // G
         for sl, nk in _row_groups(rows, n, sp.causal):
-            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal)
+            p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal, sp.window)
             dp = dattn[sl, hq] @ v[:nk, kv].T
             dv[:nk, kv] += p.T @ dattn[sl, hq]
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))

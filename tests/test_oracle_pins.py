@@ -25,9 +25,9 @@ torch.set_default_dtype(torch.float64)
 
 
 def _shape(name="t", s=8, h=8, H=2, Hkv=2, d=4, f=16, norm="layernorm", ffn="gelu",
-           bias=True, rope=None, causal=True):
+           bias=True, rope=None, causal=True, window=0):
     return wl.LayerShape(name, 9, "f32", 1, s, h, H, Hkv, d, f, norm, ffn, bias, causal, rope,
-                         s, s, H)
+                         s, s, H, window=window)
 
 
 def _weights(sh, seed_shift=0):
@@ -47,6 +47,8 @@ VARIANTS = {
                                    rope=10000.0),
     "llama-gqa-swiglu": dict(norm="rmsnorm", ffn="swiglu", bias=False, H=4, Hkv=1, h=16),
     "noncausal-gelu": dict(norm="layernorm", ffn="gelu", bias=True, causal=False),
+    "window-gqa-rope": dict(norm="rmsnorm", ffn="swiglu", bias=False, H=4, Hkv=2, h=16,
+                            rope=10000.0, window=3),
 }
 
 
@@ -76,8 +78,15 @@ def _torch_layer(x, w, sh):
     G = H // Hkv
     k = k.repeat_interleave(G, dim=2)
     v = v.repeat_interleave(G, dim=2)
-    o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
-                                       is_causal=sh.causal)
+    if sh.window:
+        i = torch.arange(s)[:, None]
+        j = torch.arange(s)[None, :]
+        mask = (j <= i) & (i - j < sh.window)
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2),
+                                           v.transpose(1, 2), attn_mask=mask)
+    else:
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2),
+                                           v.transpose(1, 2), is_causal=sh.causal)
     o = o.transpose(1, 2).reshape(b, s, H * d)
     h1 = x + F.linear(o, w["w_o"].T, w.get("b_o"))
     if sh.norm == "layernorm":
@@ -393,3 +402,26 @@ def test_stack_central_differences():
     one = orc.stack(x, ws[:1], sp, dy=dy)
     ref = orc.layer(x, ws[0], sp, dy=dy)
     assert np.array_equal(one["y"], ref["y"]) and np.array_equal(one["dx"], ref["dx"])
+
+
+def test_sliding_window_closed_forms():
+    """Window 1: each row sees only itself, so the attention output of a row
+    is that row's value vector; a window of s or more is plain causal
+    attention, bit for bit."""
+    sh = _shape(s=12, d=4, f=16, window=1)
+    w = _weights(sh)
+    x, dy = _inputs(sh)
+    w0 = dict(w)
+    w0["w_o"] = np.eye(w["w_o"].shape[0])
+    w0["b_o"] = np.zeros_like(w["b_o"])
+    w0["w_2"] = np.zeros_like(w["w_2"])
+    w0["b_2"] = np.zeros_like(w["b_2"])
+    y = orc.layer(x, w0, orc.spec_of(sh))["y"]
+    xn, _, _ = orc.norm_forward(x[0], w["n1_g"], w["n1_b"], "layernorm", 1e-5)
+    H, d = sh.n_heads, sh.head_dim
+    v = (xn @ w["w_qkv"] + w["b_qkv"])[:, 2 * H * d:]
+    assert np.max(np.abs((y[0] - x[0]) - v)) < 1e-12
+    full = _shape(s=12, d=4, f=16)
+    a = orc.layer(x, w, orc.spec_of(full), dy=dy)
+    b = orc.layer(x, w, orc.spec_of(full.replace(window=12)), dy=dy)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["dx"], b["dx"])

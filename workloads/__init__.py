@@ -64,6 +64,7 @@ class LayerShape:
     kv_block: int
     head_chunk: int
     norm_eps: float = 1e-5
+    window: int = 0          # causal sliding window (0: none)
 
     def replace(self, **kw) -> "LayerShape":
         return dataclasses.replace(self, **kw)
