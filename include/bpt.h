@@ -90,7 +90,11 @@ typedef struct {
   int64_t head_chunk;  /* U: query heads per stage; divides H and is a multiple of H / n_kv_heads */
   double rope_base;    /* e.g. 500000.0 */
   float norm_eps;      /* e.g. 1e-5 */
-  int32_t reserved;
+  int32_t window;      /* causal sliding window W >= 1 (key j visible to query i iff
+                          i - W < j <= i; requires causal = 1), or 0 for none. A positional
+                          bias of -inf outside the window ("Blockwise Parallel Transformer...",
+                          §3.4: the bias generated from query and key block positions); key
+                          blocks wholly outside every row's window are skipped. */
 } bpt_layer_desc;
 
 /* Layer weights, storage dtype. w_qkv is [h, (H + 2 n_kv_heads) d] packed Q | K | V, head k in

@@ -52,7 +52,7 @@ class BptLayerDesc(ctypes.Structure):
         ("n_heads", ctypes.c_int64), ("n_kv_heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
         ("ffn_dim", ctypes.c_int64), ("q_block", ctypes.c_int64), ("kv_block", ctypes.c_int64),
         ("head_chunk", ctypes.c_int64), ("rope_base", ctypes.c_double),
-        ("norm_eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float), ("window", ctypes.c_int32),
     ]
 
 
@@ -181,6 +181,7 @@ class LayerConfig:
     head_chunk: Optional[int] = None
     batch: int = 1
     norm_eps: float = 1e-5
+    window: int = 0
 
     @staticmethod
     def from_shape(sh) -> "LayerConfig":
@@ -188,7 +189,8 @@ class LayerConfig:
                            n_kv_heads=sh.n_kv_heads, head_dim=sh.head_dim, ffn_dim=sh.ffn_dim,
                            dtype=sh.dtype, norm=sh.norm, ffn=sh.ffn, causal=sh.causal,
                            rope_base=sh.rope_base, q_block=sh.q_block, kv_block=sh.kv_block,
-                           head_chunk=sh.head_chunk, batch=sh.batch, norm_eps=sh.norm_eps)
+                           head_chunk=sh.head_chunk, batch=sh.batch, norm_eps=sh.norm_eps,
+                           window=getattr(sh, "window", 0))
 
     def desc(self) -> BptLayerDesc:
         return BptLayerDesc(
@@ -198,7 +200,7 @@ class LayerConfig:
             n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, ffn_dim=self.ffn_dim,
             q_block=self.q_block, kv_block=self.kv_block,
             head_chunk=self.head_chunk if self.head_chunk else self.n_heads,
-            rope_base=float(self.rope_base or 0.0), norm_eps=self.norm_eps, reserved=0)
+            rope_base=float(self.rope_base or 0.0), norm_eps=self.norm_eps, window=self.window)
 
 
 def _desc(d) -> BptLayerDesc:

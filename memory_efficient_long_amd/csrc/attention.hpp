@@ -41,6 +41,7 @@ struct AttnFwdArgs {
   T* o; int64_t ldo;                    // token-major; head hq at column hq * D
   float* lse;                           // [nh, s], base 2
   int s, nh, group, causal;
+  int window;                           // causal sliding window W (0: none): keys i - W < j <= i
   float scale_log2;                     // log2(e) / sqrt(D)
 };
 
@@ -53,6 +54,7 @@ struct AttnBwdArgs {
   T* dk; T* dv; int64_t lddkv;          // token-major, KV head hk at column hk * D
   const float2* rope;                   // cos/sin [s, D/2] or null
   int s, nh, nkv, group, causal;
+  int window;                           // as in AttnFwdArgs
   float scale_log2, scale;              // log2(e)/sqrt(D), 1/sqrt(D)
   // dK/dV split over the query heads of a KV head (bf16 head_dim 64/128):
   // nparts > 1 runs nparts workgroups per key tile, each over group / nparts
@@ -198,6 +200,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+  // Sliding window: key tiles wholly before every row's window are skipped.
+  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
+  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
 
   RowTile<T, BKV, D> kt, vtile;
   f32x16 oacc[ND];
@@ -206,23 +211,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  if (ntiles > 0) {
-    kt.load(Kp, D, 0, s, tid);
-    vtile.load(Vp, D, 0, s, tid);
+  if (ntiles > t_lo) {
+    kt.load(Kp, D, t_lo * BKV, s, tid);
+    vtile.load(Vp, D, t_lo * BKV, s, tid);
     kt.store_swz(ks[0], tid);
     vtile.store_cols(vt[0], LDV, tid);
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t_lo; t < ntiles; ++t) {
+    const int buf = (t - t_lo) & 1;
     if (t + 1 < ntiles) {
       kt.load(Kp, D, (t + 1) * BKV, s, tid);
       vtile.load(Vp, D, (t + 1) * BKV, s, tid);
     }
-    if (wave_active && t < wave_tiles) {
+    if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
-      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
+                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -232,13 +238,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
           sacc[sb] = mma(kf, qf[c], sacc[sb]);
         }
       }
-      if (MASK) {  // wave-uniform; keys past min(query, s - 1) get -inf
-        const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb;
+      if (MASK) {  // wave-uniform; keys past min(query, s - 1), or W or more before it, get -inf
+        const int qc = a.causal ? min(qrow, s - 1) : s - 1;
+        const int lim = qc - kvb;
+        const int lo = a.window ? qc - a.window - kvb : -BKV;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[sb][r] = (32 * sb + acc_row(r, g) > lim) ? -INFINITY : sacc[sb][r];
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * sb + acc_row(r, g);
+            sacc[sb][r] = (off > lim || off <= lo) ? -INFINITY : sacc[sb][r];
+          }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -249,7 +259,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       // Move the running max only when this tile exceeds it by > 8 (log2 units).
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        // The branch is wave-wide: with a window, a row may still have seen no
+        // visible key (m_run = m_new = -inf); it keeps its (zero) state.
+        const float alpha = a.window && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < ND; ++i)
@@ -257,12 +269,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         m_run = m_new;
       }
+      // A row whose keys so far are all outside its window keeps m_run = -inf;
+      // its masked scores then give exp2(-inf) = 0 rather than exp2(NaN).
+      const float m_sub = a.window && m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[sb][r], sl2, -m_run));
+          const float p = fast_exp2(fmaf(sacc[sb][r], sl2, -m_sub));
           sacc[sb][r] = p;
           rs += p;
         }
@@ -343,7 +358,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
   const float sl2 = a.scale_log2;
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
-  const int per_head = nqt - qt0;
+  // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
+  const int qt1 = a.window ? min(nqt, (kv0 + BKV + a.window - 2) / BQ + 1) : nqt;
+  const int per_head = qt1 - qt0;
   const int nsteps = per_head * a.group;
 
   RowTile<T, BQ, D> qtile, dotile;
@@ -384,7 +401,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
     const float* ddb = dd_s[buf];
 
     // Steps touching the diagonal (or the sequence end) need the mask.
-    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
+    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s ||
+                      (a.window && q0 + BQ - 1 >= kv0 + a.window);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S = Q K^T and dP = dO V^T for this wave's 32 keys (lane = key).
@@ -407,12 +425,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
         sacc[r] = p;
         dpacc[r] = p * (dpacc[r] - d4[r >> 2][r & 3]);
       }
-      // Causal / tail mask: key row must be <= min(query, s - 1).
-      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s)) {
+      // Causal / tail / window mask: key row must be <= min(query, s - 1) and,
+      // with a window, more than query - W.
+      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s ||
+                   (a.window && q0 + 32 * qb + 31 >= kv0 + 32 * w + a.window))) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qg = q0 + 32 * qb + acc_row(r, g);
-          const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1);
+          const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1) ||
+                              (a.window && kvrow <= qg - a.window);
           sacc[r] = masked ? 0.f : sacc[r];
           dpacc[r] = masked ? 0.f : dpacc[r];
         }
@@ -502,6 +523,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
+  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
   const float sl2 = a.scale_log2;
 
   RowTile<T, BKV, D> ktile, vtile;
@@ -509,11 +532,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) dqacc[i] = zero16();
 
-  if (ntiles > 0) {
-    ktile.load(Kp, D, 0, s, tid);
-    vtile.load(Vp, D, 0, s, tid);
+  if (ntiles > t_lo) {
+    ktile.load(Kp, D, t_lo * BKV, s, tid);
+    vtile.load(Vp, D, t_lo * BKV, s, tid);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < ntiles; ++t) {
     __syncthreads();
     ktile.store_swz(ks, tid);
     ktile.store_cols(kts, LDT, tid);
@@ -523,9 +546,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
       ktile.load(Kp, D, (t + 1) * BKV, s, tid);
       vtile.load(Vp, D, (t + 1) * BKV, s, tid);
     }
-    if (wave_active && t < wave_tiles) {
+    if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
-      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
+                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         // S^T = K Q^T and dP^T = V dO^T (lane = query row).
@@ -540,10 +564,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
           const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
           dpacc[r] = p * (dpacc[r] - dd_q);
         }
-        if (MASK) {  // wave-uniform; keys past min(query, s - 1) contribute nothing
-          const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb - 32 * sb;
+        if (MASK) {  // wave-uniform; keys outside [query - W + 1, min(query, s - 1)] contribute nothing
+          const int qc = a.causal ? min(qrow, s - 1) : s - 1;
+          const int lim = qc - kvb - 32 * sb;
+          const int lo = a.window ? qc - a.window - kvb - 32 * sb : -BKV;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dpacc[r] = (acc_row(r, g) > lim) ? 0.f : dpacc[r];
+          for (int r = 0; r < 16; ++r)
+            dpacc[r] = (acc_row(r, g) > lim || acc_row(r, g) <= lo) ? 0.f : dpacc[r];
         }
         // dQ^T += K^T dS^T over this block's 32 keys (two 16-key chunks).
 #pragma unroll

@@ -180,6 +180,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+  // Sliding window: key tiles wholly before every row's window are skipped
+  // (the workgroup's first row bounds t_lo, each wave's its own).
+  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
+  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -190,9 +194,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
   const uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
   const typename TL::template Loader<BKV, 4> kvld(D, lane);
-  if (ntiles > 0) {
-    kvld.issue(ksa, Kp, 0, s, w, lane);
-    kvld.issue(vsa, Vp, 0, s, w, lane);
+  if (ntiles > t_lo) {
+    kvld.issue(ksa, Kp, t_lo * BKV, s, w, lane);
+    kvld.issue(vsa, Vp, t_lo * BKV, s, w, lane);
   }
   wait_dma();
   __syncthreads();
@@ -206,22 +210,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
       kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
     }
-    if (wave_active && t < wave_tiles) {
+    if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
-      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
+                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
           sacc[sb] = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc[sb]);
-      if (MASK) {  // wave-uniform; keys past min(query, s - 1) get -inf
-        const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb;
+      if (MASK) {  // wave-uniform; keys past min(query, s - 1), or W or more before it, get -inf
+        const int qc = a.causal ? min(qrow, s - 1) : s - 1;
+        const int lim = qc - kvb;
+        const int lo = a.window ? qc - a.window - kvb : -BKV;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[sb][r] = (32 * sb + acc_row(r, g) > lim) ? -INFINITY : sacc[sb][r];
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * sb + acc_row(r, g);
+            sacc[sb][r] = (off > lim || off <= lo) ? -INFINITY : sacc[sb][r];
+          }
       }
       // A query's 64 keys of the tile are split between lanes l and l + 32;
       // each half tests its own maximum (the running max is common to both),
@@ -235,7 +244,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       mx *= sl2;
       if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
         const float m_new = fmaxf(m_run, fmaxf(mx, shfl_xor(mx, 32)));
-        const float alpha = fast_exp2(m_run - m_new);
+        // The branch is wave-wide: with a window, a row may still have seen no
+        // visible key (m_run = m_new = -inf); it keeps its (zero) state.
+        const float alpha = a.window && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < ND; ++i)
@@ -243,10 +254,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         m_run = m_new;
       }
+      // A row whose keys so far are all outside its window keeps m_run = -inf;
+      // its masked scores then give exp2(-inf) = 0 rather than exp2(NaN).
+      const float m_sub = a.window && m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], sl2, -m_run));
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], sl2, -m_sub));
       // P in bf16 (the B operand of O^T += V^T P^T); the row sum is taken
       // over the same bf16 values, two per dot-product instruction, so the
       // normaliser matches what the MFMAs accumulate.
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
     wait_dma();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_lo; t < ntiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>());
     if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }
@@ -357,7 +371,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const float sl2 = a.scale_log2, inv_sl2 = 1.f / a.scale_log2;
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
-  const int per_head = nqt - qt0;
+  // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
+  const int qt1 = a.window ? min(nqt, (kv0 + BKV + a.window - 2) / BQ + 1) : nqt;
+  const int per_head = qt1 - qt0;
   const int nsteps = per_head * gp;
 
   // Row statistics of the next step: loaded raw (before the tile loads, so
@@ -403,7 +419,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     const int q0 = (qt0 + step % per_head) * BQ;
     asm volatile("" : "+v"(rf), "+v"(trb));
     if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
-    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s;
+    const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s ||
+                      (a.window && q0 + BQ - 1 >= kv0 + a.window);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // Seeding the accumulators with -lse (score units) and -D_i puts the row
@@ -452,11 +469,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         sacc[r] = p;
         dpacc[r] = p * dpacc[r];
       }
-      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s)) {
+      if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s ||
+                   (a.window && q0 + 32 * qb + 31 >= kv0 + 32 * w + a.window))) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qg = q0 + 32 * qb + acc_row(r, g);
-          const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1);
+          const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1) ||
+                              (a.window && kvrow <= qg - a.window);
           sacc[r] = masked ? 0.f : sacc[r];
           dpacc[r] = masked ? 0.f : dpacc[r];
         }
@@ -606,6 +625,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
+  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
+  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
   const float sl2 = a.scale_log2;
 
   f32x16 dqacc[ND];
@@ -615,9 +636,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
   uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
   const typename TL::template Loader<BKV, 4> kvld(D, lane);
-  if (ntiles > 0) {
-    kvld.issue(ksa, Kp, 0, s, w, lane);
-    kvld.issue(vsa, Vp, 0, s, w, lane);
+  if (ntiles > t_lo) {
+    kvld.issue(ksa, Kp, t_lo * BKV, s, w, lane);
+    kvld.issue(vsa, Vp, t_lo * BKV, s, w, lane);
   }
   wait_dma();
   __syncthreads();
@@ -633,9 +654,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
       kvld.issue(ksa + (buf ^ 1) * TB, Kp, (t + 1) * BKV, s, w, lane);
       kvld.issue(vsa + (buf ^ 1) * TB, Vp, (t + 1) * BKV, s, w, lane);
     }
-    if (wave_active && t < wave_tiles) {
+    if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
-      const bool MASK = a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s);
+      const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
+                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc.
@@ -650,9 +672,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
 #pragma unroll
         for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(fmaf(sacc[r], sl2, -lse_q));
         if (MASK) {
-          const int lim = (a.causal ? min(qrow, s - 1) : s - 1) - kvb - 32 * sb;
+          const int qc = a.causal ? min(qrow, s - 1) : s - 1;
+          const int lim = qc - kvb - 32 * sb;
+          const int lo = a.window ? qc - a.window - kvb - 32 * sb : -BKV;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dpacc[r] = (acc_row(r, g) > lim) ? 0.f : dpacc[r];
+          for (int r = 0; r < 16; ++r)
+            dpacc[r] = (acc_row(r, g) > lim || acc_row(r, g) <= lo) ? 0.f : dpacc[r];
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -669,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
     wait_dma();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_lo; t < ntiles; t += 2) {
     tile_step(t, std::integral_constant<int, 0>());
     if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>());
   }

@@ -112,7 +112,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ----------------------------------------------------------------- plan
 struct Plan {
-  int dtype, norm, ffn, causal, rope;
+  int dtype, norm, ffn, causal, rope, window;
   int64_t b, s, h, H, Hkv, D, f, cq, ckv, U, G, nkvc, qkv_cols, chunk_cols;
   int64_t gq;  // query blocks per weight-gradient group (backward)
   double rope_base;
@@ -154,10 +154,13 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
   if (d->use_rope && !(d->rope_base > 1.0 && std::isfinite(d->rope_base)))
     return fail(BPT_EINVAL, "rope_base");
   if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(BPT_EINVAL, "norm_eps");
+  if (d->window < 0) return fail(BPT_EINVAL, "window must be >= 0");
+  if (d->window > 0 && !d->causal) return fail(BPT_EINVAL, "a sliding window requires causal = 1");
   const int64_t qkv_cols = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
   if (d->seq_len * std::max<int64_t>(std::max(d->hidden, qkv_cols), d->ffn_dim) >= (int64_t(1) << 40))
     return fail(BPT_EUNSUPPORTED, "problem too large");
   p.dtype = d->dtype; p.norm = d->norm; p.ffn = d->ffn; p.causal = d->causal; p.rope = d->use_rope;
+  p.window = d->window;
   p.b = d->batch; p.s = d->seq_len; p.h = d->hidden; p.H = d->n_heads; p.Hkv = d->n_kv_heads;
   p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
   p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
@@ -512,7 +515,7 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
                     float* lse) {
   AttnFwdArgs<T> a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.ldo = p.H * p.D; a.lse = lse;
-  a.s = (int)p.s; a.nh = (int)p.U; a.group = (int)p.G; a.causal = p.causal;
+  a.s = (int)p.s; a.nh = (int)p.U; a.group = (int)p.G; a.causal = p.causal; a.window = p.window;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
@@ -535,6 +538,7 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.lddo = p.H * p.D; a.lse = lse; a.dvec = dvec;
   a.dq = dq; a.lddq = p.chunk_cols; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
   a.s = (int)p.s; a.nh = (int)p.U; a.nkv = (int)p.nkvc; a.group = (int)p.G; a.causal = p.causal;
+  a.window = p.window;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   a.scale = (float)(1.0 / std::sqrt((double)p.D));
   const dim3 gkv((unsigned)(p.nkvc * ((p.s + 127) / 128))), gq((unsigned)(p.U * ((p.s + 127) / 128)));

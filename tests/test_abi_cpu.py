@@ -97,6 +97,7 @@ def test_workloads_validate(name):
     ("head_chunk", 3, 1), ("head_chunk", 0, 1), ("norm_eps", float("nan"), 1),
     # the norm kernels take rows of at most 16384 elements
     ("hidden", 32768, 3),
+    ("window", -1, 1),
 ])
 def test_invalid_descriptors(field, value, status):
     d = _desc(**{field: value})
@@ -388,3 +389,9 @@ def test_stack_descriptor_rules():
 def dataclasses_replace(obj, **kw):
     import dataclasses
     return dataclasses.replace(obj, **kw)
+
+
+def test_window_needs_causal():
+    assert bpt.bpt_layer_validate(_desc(window=64)) == 0
+    assert bpt.bpt_layer_validate(_desc(window=1 << 30)) == 0      # wider than s: plain causal
+    assert bpt.bpt_layer_validate(_desc(window=64, causal=0)) == 1

@@ -179,6 +179,25 @@ def test_split_k_weight_gradients_and_ffn_groups_match_oracle():
     _check(errs, sh.dtype)
 
 
+def test_window_edge_cases():
+    """Window 1 (each row attends only to itself) against the oracle, and a
+    window of s or more giving plain causal attention bit for bit."""
+    sh = wl.SMALL["bf16-d128-window"].replace(name="bf16-d128-window1", window=1)
+    _say(f"[window] {sh.name} W=1")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    errs = compare(run_gpu(inp), run_oracle(inp), sh.dtype, residual_x=inp.x.f64(),
+                   dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+    causal = sh.replace(window=0)
+    wide = sh.replace(window=sh.seq_len)
+    a = run_gpu(inp, cfg=__import__("memory_efficient_long_amd").LayerConfig.from_shape(causal))
+    b = run_gpu(inp, cfg=__import__("memory_efficient_long_amd").LayerConfig.from_shape(wide))
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["dx"], b["dx"])
+    for k in a["grads"]:
+        assert np.array_equal(a["grads"][k], b["grads"][k]), k
+
+
 # ----------------------------------------------------------------- peaked softmax
 def _base_d128(causal):
     return wl.WORKLOADS["gpt1b-s8k"].replace(
@@ -290,6 +309,24 @@ def test_dense_long_sequence_head_dim_128():
     inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
     gpu = run_gpu(inp)
     _say("  gpu done; oracle ...")
+    ref = run_oracle(inp)
+    errs = compare(gpu, ref, sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_dense_long_sequence_window():
+    """A causal sliding window of 2000 keys at s = 16384, head_dim 128, dense
+    cotangent: every query tile of the attention kernels starts its key loop
+    at its window's first tile and masks the boundary tiles."""
+    sh = wl.WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d128-s16k-window", seq_len=16384, hidden=256, n_heads=2, n_kv_heads=2,
+        head_dim=128, ffn_dim=512, q_block=4096, kv_block=8192, head_chunk=2, window=2000)
+    _say(f"[dense-window] s={sh.seq_len} W={sh.window}")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    gpu = run_gpu(inp)
     ref = run_oracle(inp)
     errs = compare(gpu, ref, sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
     _say(f"  errs {_fmt(errs)}")

@@ -138,6 +138,21 @@ SMALL: Dict[str, LayerShape] = {
     "bf16-d32": WORKLOADS["gpt1b-s8k"].replace(
         name="bf16-d32", seq_len=272, hidden=128, n_heads=4, n_kv_heads=4, head_dim=32,
         ffn_dim=512, q_block=136, kv_block=272, head_chunk=2),
+    # Causal sliding windows (not multiples of the 64-key tiles): the DMA
+    # kernels at head_dim 128 and at 64 with GQA (the query-head-split dK/dV
+    # pass), the register kernels in bf16 (head_dim 32) and fp32.
+    "bf16-d128-window": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d128-window", seq_len=1040, hidden=256, n_heads=2, n_kv_heads=2,
+        head_dim=128, ffn_dim=512, q_block=520, kv_block=1040, head_chunk=2, window=200),
+    "bf16-d64-gqa-rope-window": WORKLOADS["llama8b-s64k"].replace(
+        name="bf16-d64-gqa-rope-window", seq_len=1040, hidden=256, n_heads=4, n_kv_heads=2,
+        head_dim=64, ffn_dim=768, q_block=520, kv_block=1040, head_chunk=2, window=100),
+    "bf16-d32-window": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d32-window", seq_len=528, hidden=128, n_heads=4, n_kv_heads=4, head_dim=32,
+        ffn_dim=512, q_block=264, kv_block=528, head_chunk=2, window=33),
+    "f32-d64-window": WORKLOADS["gpt-tiny-fp32"].replace(
+        name="f32-d64-window", seq_len=400, hidden=128, n_heads=2, n_kv_heads=2, head_dim=64,
+        ffn_dim=256, q_block=200, kv_block=400, head_chunk=2, window=77),
     "f32-d64-gqa-rope-noncausal": WORKLOADS["gpt-tiny-fp32"].replace(
         name="f32-d64-gqa-rope-noncausal", seq_len=240, hidden=256, n_heads=4, n_kv_heads=2,
         head_dim=64, ffn_dim=512, norm="rmsnorm", ffn="gelu", causal=False,
