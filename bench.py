@@ -29,8 +29,14 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
-def attn_pairs(s: int, causal: bool) -> int:
-    return s * (s + 1) // 2 if causal else s * s
+def attn_pairs(s: int, causal: bool, window: int = 0) -> int:
+    """Visible (query, key) pairs per head: causal rows see i + 1 keys, or
+    min(i + 1, W) with a sliding window W."""
+    if not causal:
+        return s * s
+    if window and window < s:
+        return window * (window + 1) // 2 + (s - window) * window
+    return s * (s + 1) // 2
 
 
 def model_flops(sh) -> dict:
@@ -39,9 +45,10 @@ def model_flops(sh) -> dict:
     s, h, H, Hkv, d, f = sh.seq_len, sh.hidden, sh.n_heads, sh.n_kv_heads, sh.head_dim, sh.ffn_dim
     n_ffn = 3 if sh.ffn == "swiglu" else 2
     lin = 2 * s * h * (H + 2 * Hkv) * d + 2 * s * H * d * h + 2 * s * h * f * n_ffn
-    attn = 4 * d * H * attn_pairs(s, sh.causal)
+    w = getattr(sh, "window", 0)
+    attn = 4 * d * H * attn_pairs(s, sh.causal, w)
     fwd = (lin + attn) * sh.batch
-    pairs = attn_pairs(s, sh.causal) * sh.batch
+    pairs = attn_pairs(s, sh.causal, w) * sh.batch
     return {"fwd": fwd, "step": 3 * fwd,
             # attention units (see ROOFLINE_UNITS): forward QK^T and PV, 4d per
             # visible pair and head; backward dV, dP, dK and dQ, 8d
@@ -422,6 +429,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="causal sliding window of W keys (local attention)")
     ap.add_argument("--stack", type=int, default=0, metavar="L",
                     help="time a stack of L layers of the workload's shape instead of one layer")
     ap.add_argument("--checkpoint-every", type=int, default=1, metavar="K",
@@ -472,6 +481,8 @@ def main() -> int:
     sh = wl.WORKLOADS[args.workload]
     if args.head_chunk:
         sh = sh.replace(head_chunk=args.head_chunk)
+    if args.window:
+        sh = sh.replace(window=args.window)
     cfg = bpt.LayerConfig.from_shape(sh)
     desc = cfg.desc()
     dev = torch.device("cuda:0")
@@ -600,7 +611,8 @@ def main() -> int:
                    "hidden": sh.hidden, "n_heads": sh.n_heads, "n_kv_heads": sh.n_kv_heads,
                    "head_dim": sh.head_dim, "ffn_dim": sh.ffn_dim, "ffn": sh.ffn, "norm": sh.norm,
                    "causal": sh.causal, "rope_base": sh.rope_base, "q_block": sh.q_block,
-                   "kv_block": sh.kv_block, "head_chunk": sh.head_chunk},
+                   "kv_block": sh.kv_block, "head_chunk": sh.head_chunk,
+                   "window": sh.window},
         "ms_per_step_median": round(float(np.median(step_ms)), 3),
         "ms_per_step_min": round(float(np.min(step_ms)), 3),
         "model_tflops": round(tflops, 2),

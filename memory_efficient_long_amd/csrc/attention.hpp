@@ -169,8 +169,9 @@ __device__ __forceinline__ typename Frag<T>::type zero_frag() {
 template <typename T> constexpr int pad_t() { return sizeof(T) == 2 ? 4 : 4; }
 
 // ============================================================================ forward
-template <typename T, int D>
+template <typename T, int D, bool WIN = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 128, BKV = 64;
   constexpr int LDV = BKV + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
   // Sliding window: key tiles wholly before every row's window are skipped.
-  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
-  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
+  const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
+  const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
 
   RowTile<T, BKV, D> kt, vtile;
   f32x16 oacc[ND];
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
     if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
       const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
-                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
+                        (win && kvb <= q0 + 32 * w + 31 - win);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       if (MASK) {  // wave-uniform; keys past min(query, s - 1), or W or more before it, get -inf
         const int qc = a.causal ? min(qrow, s - 1) : s - 1;
         const int lim = qc - kvb;
-        const int lo = a.window ? qc - a.window - kvb : -BKV;
+        const int lo = win ? qc - win - kvb : -BKV;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
         const float m_new = fmaxf(m_run, mx);
         // The branch is wave-wide: with a window, a row may still have seen no
         // visible key (m_run = m_new = -inf); it keeps its (zero) state.
-        const float alpha = a.window && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        const float alpha = win && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < ND; ++i)
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       }
       // A row whose keys so far are all outside its window keeps m_run = -inf;
       // its masked scores then give exp2(-inf) = 0 rather than exp2(NaN).
-      const float m_sub = a.window && m_run == -INFINITY ? 0.f : m_run;
+      const float m_sub = win && m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -319,8 +320,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
 }
 
 // ============================================================================ backward: dK, dV
-template <typename T, int D>
+template <typename T, int D, bool WIN = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 64, BKV = 128;
   constexpr int LDT = BQ + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
   // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
-  const int qt1 = a.window ? min(nqt, (kv0 + BKV + a.window - 2) / BQ + 1) : nqt;
+  const int qt1 = win ? min(nqt, (kv0 + BKV + win - 2) / BQ + 1) : nqt;
   const int per_head = qt1 - qt0;
   const int nsteps = per_head * a.group;
 
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
 
     // Steps touching the diagonal (or the sequence end) need the mask.
     const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s ||
-                      (a.window && q0 + BQ - 1 >= kv0 + a.window);
+                      (win && q0 + BQ - 1 >= kv0 + win);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S = Q K^T and dP = dO V^T for this wave's 32 keys (lane = key).
@@ -428,12 +430,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
       // Causal / tail / window mask: key row must be <= min(query, s - 1) and,
       // with a window, more than query - W.
       if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s ||
-                   (a.window && q0 + 32 * qb + 31 >= kv0 + 32 * w + a.window))) {
+                   (win && q0 + 32 * qb + 31 >= kv0 + 32 * w + win))) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qg = q0 + 32 * qb + acc_row(r, g);
           const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1) ||
-                              (a.window && kvrow <= qg - a.window);
+                              (win && kvrow <= qg - win);
           sacc[r] = masked ? 0.f : sacc[r];
           dpacc[r] = masked ? 0.f : dpacc[r];
         }
@@ -485,8 +487,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
 }
 
 // ============================================================================ backward: dQ
-template <typename T, int D>
+template <typename T, int D, bool WIN = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 128, BKV = 64;
   constexpr int LDT = BKV + pad_t<T>();
   constexpr int NC = D / 16, ND = D / 32;
@@ -523,8 +526,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
-  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
-  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
+  const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
+  const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
   const float sl2 = a.scale_log2;
 
   RowTile<T, BKV, D> ktile, vtile;
@@ -549,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
     if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
       const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
-                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
+                        (win && kvb <= q0 + 32 * w + 31 - win);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         // S^T = K Q^T and dP^T = V dO^T (lane = query row).
@@ -567,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
         if (MASK) {  // wave-uniform; keys outside [query - W + 1, min(query, s - 1)] contribute nothing
           const int qc = a.causal ? min(qrow, s - 1) : s - 1;
           const int lim = qc - kvb - 32 * sb;
-          const int lo = a.window ? qc - a.window - kvb - 32 * sb : -BKV;
+          const int lo = win ? qc - win - kvb - 32 * sb : -BKV;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             dpacc[r] = (acc_row(r, g) > lim || acc_row(r, g) <= lo) ? 0.f : dpacc[r];

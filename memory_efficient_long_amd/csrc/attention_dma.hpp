@@ -148,8 +148,9 @@ struct DmaTile {
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ============================================================================ forward
-template <int D>
+template <int D, bool WIN = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
   constexpr int BQ = 128, BKV = 64;
   constexpr int NC = D / 16, ND = D / 32;
@@ -182,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
   // Sliding window: key tiles wholly before every row's window are skipped
   // (the workgroup's first row bounds t_lo, each wave's its own).
-  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
-  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
+  const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
+  const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
     if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
       const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
-                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
+                        (win && kvb <= q0 + 32 * w + 31 - win);
       f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       if (MASK) {  // wave-uniform; keys past min(query, s - 1), or W or more before it, get -inf
         const int qc = a.causal ? min(qrow, s - 1) : s - 1;
         const int lim = qc - kvb;
-        const int lo = a.window ? qc - a.window - kvb : -BKV;
+        const int lo = win ? qc - win - kvb : -BKV;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
         const float m_new = fmaxf(m_run, fmaxf(mx, shfl_xor(mx, 32)));
         // The branch is wave-wide: with a window, a row may still have seen no
         // visible key (m_run = m_new = -inf); it keeps its (zero) state.
-        const float alpha = a.window && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        const float alpha = win && m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < ND; ++i)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       }
       // A row whose keys so far are all outside its window keeps m_run = -inf;
       // its masked scores then give exp2(-inf) = 0 rather than exp2(NaN).
-      const float m_sub = a.window && m_run == -INFINITY ? 0.f : m_run;
+      const float m_sub = win && m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -321,8 +322,9 @@ __device__ __forceinline__ void seed_rows(f32x16& s, f32x16& d, float xs, float 
 // SPLIT: the query-head-split variant (a.nparts > 1, partial sums to a.part);
 // without it the part index is a compile-time zero and nothing of the split
 // remains in the code.
-template <int D, bool SPLIT = false>
+template <int D, bool SPLIT = false, bool WIN = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<bf16> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
   constexpr int BQ = 64, BKV = 128;
   constexpr int NC = D / 16, ND = D / 32;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
   // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
-  const int qt1 = a.window ? min(nqt, (kv0 + BKV + a.window - 2) / BQ + 1) : nqt;
+  const int qt1 = win ? min(nqt, (kv0 + BKV + win - 2) / BQ + 1) : nqt;
   const int per_head = qt1 - qt0;
   const int nsteps = per_head * gp;
 
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     asm volatile("" : "+v"(rf), "+v"(trb));
     if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
     const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s ||
-                      (a.window && q0 + BQ - 1 >= kv0 + a.window);
+                      (win && q0 + BQ - 1 >= kv0 + win);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // Seeding the accumulators with -lse (score units) and -D_i puts the row
@@ -470,12 +472,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         dpacc[r] = p * dpacc[r];
       }
       if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s ||
-                   (a.window && q0 + 32 * qb + 31 >= kv0 + 32 * w + a.window))) {
+                   (win && q0 + 32 * qb + 31 >= kv0 + 32 * w + win))) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qg = q0 + 32 * qb + acc_row(r, g);
           const bool masked = kvrow > (a.causal ? min(qg, s - 1) : s - 1) ||
-                              (a.window && kvrow <= qg - a.window);
+                              (win && kvrow <= qg - win);
           sacc[r] = masked ? 0.f : sacc[r];
           dpacc[r] = masked ? 0.f : dpacc[r];
         }
@@ -588,8 +590,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnBwdArgs<bf16> a) {
 }
 
 // ============================================================================ backward: dQ
-template <int D>
+template <int D, bool WIN = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf16> a) {
+  const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
   constexpr int BQ = 128, BKV = 64;
   constexpr int NC = D / 16, ND = D / 32;
@@ -625,8 +628,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   const bool wave_active = q0 + 32 * w < s;
   const int wave_last = min(q0 + 32 * w + 31, s - 1);
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
-  const int t_lo = a.window ? max(0, q0 - a.window + 1) / BKV : 0;
-  const int wave_t_lo = a.window ? max(0, q0 + 32 * w - a.window + 1) / BKV : 0;
+  const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
+  const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
   const float sl2 = a.scale_log2;
 
   f32x16 dqacc[ND];
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
     if (wave_active && t < wave_tiles && t >= wave_t_lo) {
       const int kvb = t * BKV;
       const bool MASK = (a.causal ? (kvb + BKV - 1 > q0 + 32 * w) : (kvb + BKV > s)) ||
-                        (a.window && kvb <= q0 + 32 * w + 31 - a.window);
+                        (win && kvb <= q0 + 32 * w + 31 - win);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc.
@@ -674,7 +677,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
         if (MASK) {
           const int qc = a.causal ? min(qrow, s - 1) : s - 1;
           const int lim = qc - kvb - 32 * sb;
-          const int lo = a.window ? qc - a.window - kvb - 32 * sb : -BKV;
+          const int lo = win ? qc - win - kvb - 32 * sb : -BKV;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             dpacc[r] = (acc_row(r, g) > lim || acc_row(r, g) <= lo) ? 0.f : dpacc[r];

@@ -519,12 +519,18 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
-  if constexpr (sizeof(T) == 2) {
-    if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
-    if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64>), grid, blk, 0, st, a); return check_launch("attn_fwd"); }
-  }
-  if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((attn_fwd_kernel<T, 32>), grid, blk, 0, st, a);
+  // The sliding window is a compile-time variant (WIN), so the unwindowed
+  // kernels carry none of its code.
+  auto go = [&](auto winc) {
+    constexpr bool W = decltype(winc)::value;
+    if constexpr (sizeof(T) == 2) {
+      if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128, W>), grid, blk, 0, st, a); return; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64, W>), grid, blk, 0, st, a); return; }
+    }
+    if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64, W>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, 32, W>), grid, blk, 0, st, a);
+  };
+  if (p.window) go(std::true_type()); else go(std::false_type());
   return check_launch("attn_fwd");
 }
 
@@ -545,7 +551,9 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   const dim3 blk(256);
   if (p.D == 128 && sizeof(T) != 2)
     return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
-  {
+  // The sliding window is a compile-time variant (W) of every kernel below.
+  auto dkdv_pass = [&](auto winc) {
+    constexpr bool W = decltype(winc)::value;
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DKDV, st);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
@@ -558,11 +566,11 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
       if (a.nparts > 1) a.part = dkv_part;
       const dim3 gsplit((unsigned)(wgs * a.nparts));
       if (a.nparts > 1) {
-        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, true>), gsplit, blk, 0, st, a);
-        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, true>), gsplit, blk, 0, st, a);
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, true, W>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, true, W>), gsplit, blk, 0, st, a);
       } else {
-        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128>), gsplit, blk, 0, st, a);
-        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64>), gsplit, blk, 0, st, a);
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, false, W>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, false, W>), gsplit, blk, 0, st, a);
       }
       done = p.D == 128 || p.D == 64;
       if (a.nparts > 1) {
@@ -572,23 +580,26 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
       }
     }
     if (!done) {
-      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), gkv, blk, 0, st, a);
-      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32>), gkv, blk, 0, st, a);
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64, W>), gkv, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32, W>), gkv, blk, 0, st, a);
     }
-  }
-  BPT_TRY(check_launch("attn_bwd_dkdv"));
-  {
+  };
+  auto dq_pass = [&](auto winc) {
+    constexpr bool W = decltype(winc)::value;
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DQ, st);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128>), gq, blk, 0, st, a); done = true; }
-      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<64>), gq, blk, 0, st, a); done = true; }
+      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, W>), gq, blk, 0, st, a); done = true; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<64, W>), gq, blk, 0, st, a); done = true; }
     }
     if (!done) {
-      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), gq, blk, 0, st, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32>), gq, blk, 0, st, a);
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64, W>), gq, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32, W>), gq, blk, 0, st, a);
     }
-  }
+  };
+  if (p.window) dkdv_pass(std::true_type()); else dkdv_pass(std::false_type());
+  BPT_TRY(check_launch("attn_bwd_dkdv"));
+  if (p.window) dq_pass(std::true_type()); else dq_pass(std::false_type());
   return check_launch("attn_bwd_dq");
 }
 
