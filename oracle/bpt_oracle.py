@@ -58,7 +58,7 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = ["Spec", "spec_of", "layer", "stack", "norm_forward", "norm_backward", "rope_rotate",
-           "attention_probs"]
+           "attention_probs", "philox4x32_10", "dropout_keep", "dropout_threshold"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -74,13 +74,16 @@ class Spec:
     rope_base: Optional[float] = None
     eps: float = 1e-5
     window: int = 0                # causal sliding window W (0: none)
+    dropout_p: float = 0.0         # attention-probability dropout (0: none)
+    seed: int = 0                  # 64-bit seed of the dropout masks
 
 
 def spec_of(shape) -> Spec:
     """Spec from any object carrying the layer's shape attributes."""
     return Spec(shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
                 shape.norm, shape.ffn, shape.causal, shape.rope_base,
-                getattr(shape, "norm_eps", 1e-5), getattr(shape, "window", 0))
+                getattr(shape, "norm_eps", 1e-5), getattr(shape, "window", 0),
+                getattr(shape, "dropout_p", 0.0), getattr(shape, "seed", 0))
 
 
 # --------------------------------------------------------------------------- norms
@@ -157,6 +160,57 @@ def attention_probs(q_h, k_h, rows, causal, window=0):
     return e / e.sum(axis=1, keepdims=True)
 
 
+# --------------------------------------------------------------------------- dropout
+# Dropout on the attention probabilities ("Training memory", §3: the layer's
+# dropout after the softmax, whose s x s mask FlashAttention regenerates from
+# the saved random-number state instead of storing it). The mask comes from a
+# counter-based generator, Philox4x32 with 10 rounds (Salmon, Moraes, Dror and
+# Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11), so any block of
+# (query, key) pairs can be regenerated on its own: element (i, j) of head h in
+# sequence b uses the counter (i // 4, j // 4, h, b) under the key (low, high
+# 32 bits of the seed) and byte 4 (i % 4) + (j % 4) of the 16 output bytes
+# (word i % 4, little-endian byte j % 4); it is kept iff that byte is at least
+# t = round(256 p), so the effective drop probability is t / 256 and kept
+# probabilities are scaled by 256 / (256 - t).
+_PHILOX_M = (np.uint64(0xD2511F53), np.uint64(0xCD9E8D57))
+_PHILOX_W = (np.uint64(0x9E3779B9), np.uint64(0xBB67AE85))
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32-10 bijection of the 128-bit counters (c0..c3, arrays of
+    uint32 values) under the key (k0, k1): ten rounds of two 32 x 32 -> 64-bit
+    products, xors with the other counter words and the round key, and a Weyl
+    increment of the key."""
+    c0, c1, c2, c3 = (np.asarray(c, dtype=np.uint64) & _U32 for c in (c0, c1, c2, c3))
+    k0, k1 = np.uint64(k0) & _U32, np.uint64(k1) & _U32
+    for _ in range(10):
+        p0 = _PHILOX_M[0] * c0
+        p1 = _PHILOX_M[1] * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _U32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _U32
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+        k0 = (k0 + _PHILOX_W[0]) & _U32
+        k1 = (k1 + _PHILOX_W[1]) & _U32
+    return c0, c1, c2, c3
+
+
+def dropout_threshold(p):
+    return int(round(256.0 * float(p)))
+
+
+def dropout_keep(rows, n_keys, head, batch, seed, thr):
+    """Boolean keep mask [len(rows), n_keys] for query positions ``rows``."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    ii, jj = np.broadcast_arrays(i, j)
+    words = philox4x32_10(ii // 4, jj // 4, np.full(ii.shape, head), np.full(ii.shape, batch),
+                          int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)
+    w = np.choose((ii % 4).astype(np.int64), words)
+    byte = (w >> (np.uint64(8) * (jj % 4).astype(np.uint64))) & np.uint64(0xFF)
+    return byte >= np.uint64(thr)
+
+
 # Query rows per explicit score matrix. The softmax is defined row by row, so
 # evaluating the rows in groups changes nothing but the size of the temporary
 # (a group x keys matrix instead of rows x keys); with the causal mask a group
@@ -196,7 +250,7 @@ def _get(w, name, shape=None):
     return np.asarray(v, dtype=np.float64)
 
 
-def _sequence(x, w, sp: Spec, rows, dy):
+def _sequence(x, w, sp: Spec, rows, dy, batch=0):
     """One sequence. x [s, h]; rows sorted positions where y is produced and
     where the cotangent dy [len(rows), h] lives (zero elsewhere)."""
     s, h = x.shape
@@ -226,12 +280,22 @@ def _sequence(x, w, sp: Spec, rows, dy):
         q = rope_rotate(q, rows, sp.rope_base)
         k = rope_rotate(k, np.arange(n), sp.rope_base)
 
+    thr = dropout_threshold(sp.dropout_p)
+    dscale = 256.0 / (256.0 - thr)
+
+    def dropped(p, sl, nk, hq):
+        """P with the dropout mask applied (kept entries scaled); P itself
+        when there is no dropout."""
+        if not thr:
+            return p
+        return p * dropout_keep(rows[sl], nk, hq, batch, sp.seed, thr) * dscale
+
     attn = np.empty((r, H, d))
     for hq in range(H):
         kv = hq // G
         for sl, nk in _row_groups(rows, n, sp.causal):
             p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal, sp.window)
-            attn[sl, hq] = p @ v[:nk, kv]
+            attn[sl, hq] = dropped(p, sl, nk, hq) @ v[:nk, kv]
     attn2 = attn.reshape(r, H * d)
 
     h1 = x[rows] + attn2 @ w_o + (b_o if b_o is not None else 0.0)
@@ -286,8 +350,12 @@ def _sequence(x, w, sp: Spec, rows, dy):
         kv = hq // G
         for sl, nk in _row_groups(rows, n, sp.causal):
             p = attention_probs(q[sl, hq], k[:nk, kv], rows[sl], sp.causal, sp.window)
-            dp = dattn[sl, hq] @ v[:nk, kv].T
-            dv[:nk, kv] += p.T @ dattn[sl, hq]
+            pd = dropped(p, sl, nk, hq)
+            # the product with V used the dropped probabilities: its gradient
+            # reaches P through the same mask and scale
+            dpd = dattn[sl, hq] @ v[:nk, kv].T
+            dv[:nk, kv] += pd.T @ dattn[sl, hq]
+            dp = dpd if pd is p else dropped(dpd, sl, nk, hq)
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dq[sl, hq] = ds @ k[:nk, kv] / np.sqrt(d)
             dk[:nk, kv] += ds.T @ q[sl, hq] / np.sqrt(d)
@@ -333,7 +401,7 @@ def layer(x, w: Dict[str, np.ndarray], sp: Spec, dy=None, rows=None):
     rows = np.arange(s) if rows is None else np.asarray(sorted(set(int(i) for i in rows)))
     ys, dxs, grads = [], [], {}
     for bi in range(b):
-        out = _sequence(x[bi], w, sp, rows, None if dy is None else dy[bi])
+        out = _sequence(x[bi], w, sp, rows, None if dy is None else dy[bi], batch=bi)
         ys.append(out["y"])
         if dy is not None:
             dxs.append(out["dx"])

@@ -425,3 +425,83 @@ def test_sliding_window_closed_forms():
     a = orc.layer(x, w, orc.spec_of(full), dy=dy)
     b = orc.layer(x, w, orc.spec_of(full.replace(window=12)), dy=dy)
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["dx"], b["dx"])
+
+
+# ----------------------------------------------------------------- dropout
+def test_philox_known_answers(repo_root):
+    import json
+    import os
+    kat = json.load(open(os.path.join(repo_root, "tests", "golden", "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        c = [int(x, 16) for x in v["counter"]]
+        k = [int(x, 16) for x in v["key"]]
+        out = orc.philox4x32_10(*[np.array([x]) for x in c], *k)
+        assert [int(o[0]) for o in out] == [int(x, 16) for x in v["output"]]
+
+
+def test_dropout_mask_statistics():
+    """Keep fraction within 4 standard deviations of 1 - t/256 and the bytes
+    behind the masks uniform (chi-square over 256 bins), for two heads,
+    batch entries and seeds."""
+    for p, head, batch, seed in [(0.1, 0, 0, 1), (0.5, 3, 1, 2 ** 40 + 7)]:
+        thr = orc.dropout_threshold(p)
+        keep = orc.dropout_keep(np.arange(512), 512, head, batch, seed, thr)
+        n = keep.size
+        q = 1 - thr / 256
+        assert abs(keep.mean() - q) < 4 * np.sqrt(q * (1 - q) / n)
+    # byte uniformity of the underlying generator over consecutive counters
+    c = np.arange(1 << 14)
+    words = orc.philox4x32_10(c, c * 0 + 5, c * 0, c * 0, 123, 456)
+    by = np.concatenate([(w[:, None] >> np.arange(0, 32, 8, dtype=np.uint64)) & 0xFF
+                         for w in [np.asarray(x) for x in words]]).ravel()
+    hist = np.bincount(by.astype(np.int64), minlength=256)
+    exp = by.size / 256
+    chi2 = ((hist - exp) ** 2 / exp).sum()
+    assert chi2 < 255 + 6 * np.sqrt(2 * 255)
+
+
+def _torch_attention_layer_with_masks(x, w, sh, masks, scale):
+    """The layer of _torch_layer with explicit attention (library softmax)
+    and the given dropout masks applied to the probabilities."""
+    H, Hkv, d, h = sh.n_heads, sh.n_kv_heads, sh.head_dim, sh.hidden
+    b, s, _ = x.shape
+    xn = F.layer_norm(x, (h,), w["n1_g"], w["n1_b"], eps=sh.norm_eps)
+    qkv = F.linear(xn, w["w_qkv"].T, w.get("b_qkv"))
+    q, k, v = torch.split(qkv, [H * d, Hkv * d, Hkv * d], dim=-1)
+    G = H // Hkv
+    q = q.reshape(b, s, H, d).transpose(1, 2)
+    k = k.reshape(b, s, Hkv, d).repeat_interleave(G, dim=2).transpose(1, 2)
+    v = v.reshape(b, s, Hkv, d).repeat_interleave(G, dim=2).transpose(1, 2)
+    sc = q @ k.transpose(-1, -2) / d ** 0.5
+    sc = sc.masked_fill(~torch.ones(s, s, dtype=torch.bool).tril(), float("-inf"))
+    pr = torch.softmax(sc, dim=-1) * masks * scale
+    o = (pr @ v).transpose(1, 2).reshape(b, s, H * d)
+    h1 = x + F.linear(o, w["w_o"].T, w.get("b_o"))
+    z = F.layer_norm(h1, (h,), w["n2_g"], w["n2_b"], eps=sh.norm_eps)
+    u = F.gelu(F.linear(z, w["w_1"].T, w.get("b_1")))
+    return h1 + F.linear(u, w["w_2"].T, w.get("b_2"))
+
+
+def test_dropout_matches_torch_with_the_same_masks():
+    """The layer with attention dropout equals the PyTorch composition fed the
+    oracle's masks as data (forward and autograd gradients), which pins the
+    hand-derived dropout backward; two sequences get different masks."""
+    sh = _shape(s=24, h=16, H=4, Hkv=2, d=4, f=32).replace(dropout_p=0.25, seed=99)
+    w = _weights(sh)
+    x, dy = _inputs(sh, batch=2)
+    out = orc.layer(x, w, orc.spec_of(sh), dy=dy)
+    thr = orc.dropout_threshold(sh.dropout_p)
+    masks = torch.tensor(np.stack([
+        np.stack([orc.dropout_keep(np.arange(24), 24, hq, bi, sh.seed, thr)
+                  for hq in range(sh.n_heads)]) for bi in range(2)]).astype(np.float64))
+    assert 0 < float(masks.mean()) < 1 and not torch.equal(masks[0], masks[1])
+    tw = {k: torch.tensor(v, requires_grad=True) for k, v in w.items()}
+    tx = torch.tensor(x, requires_grad=True)
+    ty = _torch_attention_layer_with_masks(tx, tw, sh, masks, 256.0 / (256 - thr))
+    assert _rel(out["y"], ty.detach().numpy()) < 1e-12
+    (ty * torch.tensor(dy)).sum().backward()
+    assert _rel(out["dx"], tx.grad.numpy()) < 1e-10
+    for name, g in out["grads"].items():
+        assert _rel(g, tw[name].grad.numpy()) < 1e-10, name
+    nodrop = orc.layer(x, w, orc.spec_of(sh.replace(dropout_p=0.0)))
+    assert _rel(out["y"], nodrop["y"]) > 1e-3

@@ -65,6 +65,8 @@ class LayerShape:
     head_chunk: int
     norm_eps: float = 1e-5
     window: int = 0          # causal sliding window (0: none)
+    dropout_p: float = 0.0   # attention-probability dropout (0: none)
+    seed: int = 0            # dropout seed
 
     def replace(self, **kw) -> "LayerShape":
         return dataclasses.replace(self, **kw)
