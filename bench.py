@@ -431,6 +431,8 @@ def main() -> int:
                     help="also time GEMM and row-wise kernel classes (adds events)")
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="causal sliding window of W keys (local attention)")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="attention dropout probability (masks regenerated in the backward)")
     ap.add_argument("--stack", type=int, default=0, metavar="L",
                     help="time a stack of L layers of the workload's shape instead of one layer")
     ap.add_argument("--checkpoint-every", type=int, default=1, metavar="K",
@@ -483,6 +485,8 @@ def main() -> int:
         sh = sh.replace(head_chunk=args.head_chunk)
     if args.window:
         sh = sh.replace(window=args.window)
+    if args.dropout:
+        sh = sh.replace(dropout_p=args.dropout, seed=1234)
     cfg = bpt.LayerConfig.from_shape(sh)
     desc = cfg.desc()
     dev = torch.device("cuda:0")
@@ -612,7 +616,7 @@ def main() -> int:
                    "head_dim": sh.head_dim, "ffn_dim": sh.ffn_dim, "ffn": sh.ffn, "norm": sh.norm,
                    "causal": sh.causal, "rope_base": sh.rope_base, "q_block": sh.q_block,
                    "kv_block": sh.kv_block, "head_chunk": sh.head_chunk,
-                   "window": sh.window},
+                   "window": sh.window, "dropout_p": sh.dropout_p},
         "ms_per_step_median": round(float(np.median(step_ms)), 3),
         "ms_per_step_min": round(float(np.min(step_ms)), 3),
         "model_tflops": round(tflops, 2),

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define BPT_ABI_VERSION 1
+#define BPT_ABI_VERSION 2
 
 typedef enum {
   BPT_OK = 0,
@@ -95,6 +95,16 @@ typedef struct {
                           bias of -inf outside the window ("Blockwise Parallel Transformer...",
                           §3.4: the bias generated from query and key block positions); key
                           blocks wholly outside every row's window are skipped. */
+  float dropout_p;     /* dropout on the attention probabilities, in [0, 1): element (query i,
+                          key j) of global query head h in sequence b is dropped iff byte
+                          j % 4 of word i % 4 of Philox4x32-10(counter (i/4, j/4, h, b), key
+                          (seed low, seed high)) is below t = round(256 dropout_p); kept ones
+                          are scaled by 256 / (256 - t). The masks are regenerated in the
+                          backward, never stored ("Training memory...", §3: FlashAttention
+                          regenerates the dropout mask from the random-number state). 0 (or
+                          t = 0): no dropout. */
+  int32_t reserved;
+  uint64_t seed;       /* dropout seed */
 } bpt_layer_desc;
 
 /* Layer weights, storage dtype. w_qkv is [h, (H + 2 n_kv_heads) d] packed Q | K | V, head k in

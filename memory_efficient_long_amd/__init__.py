@@ -32,7 +32,7 @@ __all__ = [
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libbpt.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 DTYPES = {"f32": 0, "bf16": 1}
 NORMS = {"layernorm": 0, "rmsnorm": 1}
@@ -53,6 +53,7 @@ class BptLayerDesc(ctypes.Structure):
         ("ffn_dim", ctypes.c_int64), ("q_block", ctypes.c_int64), ("kv_block", ctypes.c_int64),
         ("head_chunk", ctypes.c_int64), ("rope_base", ctypes.c_double),
         ("norm_eps", ctypes.c_float), ("window", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float), ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64),
     ]
 
 
@@ -182,6 +183,8 @@ class LayerConfig:
     batch: int = 1
     norm_eps: float = 1e-5
     window: int = 0
+    dropout_p: float = 0.0
+    seed: int = 0
 
     @staticmethod
     def from_shape(sh) -> "LayerConfig":
@@ -190,7 +193,8 @@ class LayerConfig:
                            dtype=sh.dtype, norm=sh.norm, ffn=sh.ffn, causal=sh.causal,
                            rope_base=sh.rope_base, q_block=sh.q_block, kv_block=sh.kv_block,
                            head_chunk=sh.head_chunk, batch=sh.batch, norm_eps=sh.norm_eps,
-                           window=getattr(sh, "window", 0))
+                           window=getattr(sh, "window", 0),
+                           dropout_p=getattr(sh, "dropout_p", 0.0), seed=getattr(sh, "seed", 0))
 
     def desc(self) -> BptLayerDesc:
         return BptLayerDesc(
@@ -200,7 +204,8 @@ class LayerConfig:
             n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, ffn_dim=self.ffn_dim,
             q_block=self.q_block, kv_block=self.kv_block,
             head_chunk=self.head_chunk if self.head_chunk else self.n_heads,
-            rope_base=float(self.rope_base or 0.0), norm_eps=self.norm_eps, window=self.window)
+            rope_base=float(self.rope_base or 0.0), norm_eps=self.norm_eps, window=self.window,
+            dropout_p=self.dropout_p, reserved=0, seed=self.seed)
 
 
 def _desc(d) -> BptLayerDesc:

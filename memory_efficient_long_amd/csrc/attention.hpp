@@ -35,6 +35,53 @@
 
 namespace bpt {
 
+// ----------------------------------------------------------------- dropout masks
+// Dropout on the attention probabilities with masks regenerated from a
+// counter-based generator in every pass (nothing is stored): Philox4x32 with
+// ten rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11). Element (query i, key j) of global query head h in
+// sequence b takes byte j % 4 of word i % 4 of the output for the counter
+// (i / 4, j / 4, h, b) under the key (seed low, seed high); it is kept iff the
+// byte is >= thr. One call serves a 4 x 4 block of (query, key) pairs: a lane
+// that owns a query row reads one word (four consecutive keys), a lane that
+// owns a key reads one byte of each word (four consecutive queries).
+struct Philox4 { uint32_t w[4]; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {{c0, c1, c2, c3}};
+}
+
+struct DropArgs {
+  uint32_t seed_lo, seed_hi;
+  int thr;        // keep iff byte >= thr (1..255); 0: no dropout
+  float scale;    // 256 / (256 - thr), applied to kept probabilities
+  int head0;      // global index of the launch's query head 0 (head chunks)
+  int batch;      // sequence index within the batch
+};
+
+// Word `sel` (0..3) of the call for the 4 x 4 block (q4, k4) of head hg.
+__device__ __forceinline__ uint32_t drop_word(const DropArgs& d, int q4, int k4, int hg, int sel) {
+  const Philox4 r = philox4x32_10((uint32_t)q4, (uint32_t)k4, (uint32_t)hg, (uint32_t)d.batch,
+                                  d.seed_lo, d.seed_hi);
+  return sel == 0 ? r.w[0] : sel == 1 ? r.w[1] : sel == 2 ? r.w[2] : r.w[3];
+}
+
+__device__ __forceinline__ bool drop_keep_byte(uint32_t word, int byte, int thr) {
+  return (int)((word >> (8 * byte)) & 0xFFu) >= thr;
+}
+
 template <typename T>
 struct AttnFwdArgs {
   const T* q; const T* k; const T* v;  // head-major: q [nh, s, D], k/v [nkv, s, D]
@@ -43,6 +90,7 @@ struct AttnFwdArgs {
   int s, nh, group, causal;
   int window;                           // causal sliding window W (0: none): keys i - W < j <= i
   float scale_log2;                     // log2(e) / sqrt(D)
+  DropArgs drop;                        // attention dropout (used by the DROP variants)
 };
 
 template <typename T>
@@ -56,6 +104,7 @@ struct AttnBwdArgs {
   int s, nh, nkv, group, causal;
   int window;                           // as in AttnFwdArgs
   float scale_log2, scale;              // log2(e)/sqrt(D), 1/sqrt(D)
+  DropArgs drop;                        // attention dropout (used by the DROP variants)
   // dK/dV split over the query heads of a KV head (bf16 head_dim 64/128):
   // nparts > 1 runs nparts workgroups per key tile, each over group / nparts
   // of the query heads, writing raw fp32 sums to part [nparts][2][nkv][s][D]
@@ -169,7 +218,7 @@ __device__ __forceinline__ typename Frag<T>::type zero_frag() {
 template <typename T> constexpr int pad_t() { return sizeof(T) == 2 ? 4 : 4; }
 
 // ============================================================================ forward
-template <typename T, int D, bool WIN = false>
+template <typename T, int D, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 128, BKV = 64;
@@ -283,6 +332,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
           rs += p;
         }
       l_run += rs + shfl_xor(rs, 32);
+      if constexpr (DROP) {  // the normaliser above is the undropped one
+        const int hg = a.drop.head0 + hq;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wd =
+                drop_word(a.drop, qrow >> 2, (kvb + 32 * sb + 8 * j + 4 * g) >> 2, hg, qrow & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc[sb][4 * j + e] = drop_keep_byte(wd, e, a.drop.thr) ? sacc[sb][4 * j + e] : 0.f;
+          }
+      }
       // P fragments: chunk cc covers keys 16cc + {8(e/4) + 4g + e%4}.
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -305,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
   }
 
   if (wave_active && qrow < s) {
-    const float inv_l = 1.f / l_run;
+    const float inv_l = (DROP ? a.drop.scale : 1.f) / l_run;
     T* orow = a.o + (int64_t)qrow * a.ldo + (int64_t)hq * D;
 #pragma unroll
     for (int i = 0; i < ND; ++i)
@@ -320,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
 }
 
 // ============================================================================ backward: dK, dV
-template <typename T, int D, bool WIN = false>
+template <typename T, int D, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 64, BKV = 128;
@@ -421,11 +483,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
         l4[k] = ld<f32x4>(&lseb[32 * qb + 8 * k + 4 * g]);
         d4[k] = ld<f32x4>(&ddb[32 * qb + 8 * k + 4 * g]);
       }
+      if constexpr (DROP) {
+        // dV takes the kept probabilities (scaled at the end); dS = P (z dP~ - D)
+        // with z = scale for kept and 0 for dropped elements.
+        const int hg = a.drop.head0 + hk * a.group + step / per_head;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[r], sl2, -l4[r >> 2][r & 3]));
-        sacc[r] = p;
-        dpacc[r] = p * (dpacc[r] - d4[r >> 2][r & 3]);
+        for (int j = 0; j < 4; ++j) {
+          const Philox4 rw = philox4x32_10((uint32_t)((q0 + 32 * qb + 8 * j + 4 * g) >> 2),
+                                           (uint32_t)(kvrow >> 2), (uint32_t)hg,
+                                           (uint32_t)a.drop.batch, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            const bool keep = drop_keep_byte(rw.w[e], kvrow & 3, a.drop.thr);
+            const float p = fast_exp2(fmaf(sacc[r], sl2, -l4[j][e]));
+            sacc[r] = keep ? p : 0.f;
+            dpacc[r] = p * ((keep ? a.drop.scale : 0.f) * dpacc[r] - d4[j][e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], sl2, -l4[r >> 2][r & 3]));
+          sacc[r] = p;
+          dpacc[r] = p * (dpacc[r] - d4[r >> 2][r & 3]);
+        }
       }
       // Causal / tail / window mask: key row must be <= min(query, s - 1) and,
       // with a window, more than query - W.
@@ -480,14 +562,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
       }
       if (kv < s) {
         a.dk[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = from_f32<T>(dkv);
-        a.dv[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = from_f32<T>(dvacc[i][r]);
+        a.dv[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] =
+            from_f32<T>(DROP ? dvacc[i][r] * a.drop.scale : dvacc[i][r]);
       }
     }
   }
 }
 
 // ============================================================================ backward: dQ
-template <typename T, int D, bool WIN = false>
+template <typename T, int D, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   constexpr int BQ = 128, BKV = 64;
@@ -562,10 +645,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
           sacc = mma(Swz<T, D>::frag(ks, 32 * sb + lr, 16 * c + 8 * g), qf[c], sacc);
           dpacc = mma(Swz<T, D>::frag(vs, 32 * sb + lr, 16 * c + 8 * g), df[c], dpacc);
         }
+        if constexpr (DROP) {  // dS = P (z dP~ - D), z = scale (kept) or 0
+          const int hg = a.drop.head0 + hq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
-          dpacc[r] = p * (dpacc[r] - dd_q);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wd = drop_word(a.drop, qrow >> 2, (kvb + 32 * sb + 8 * j + 4 * g) >> 2,
+                                          hg, qrow & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+              const float z = drop_keep_byte(wd, e, a.drop.thr) ? a.drop.scale : 0.f;
+              dpacc[r] = p * (z * dpacc[r] - dd_q);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+            dpacc[r] = p * (dpacc[r] - dd_q);
+          }
         }
         if (MASK) {  // wave-uniform; keys outside [query - W + 1, min(query, s - 1)] contribute nothing
           const int qc = a.causal ? min(qrow, s - 1) : s - 1;

@@ -148,7 +148,7 @@ struct DmaTile {
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ============================================================================ forward
-template <int D, bool WIN = false>
+template <int D, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
@@ -276,6 +276,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       // this half's 32 keys; the halves share the running max and are added
       // once, after the last tile
       l_run += row_sum_bf16x32(pf);
+      if constexpr (DROP) {
+        // The normaliser above is the undropped one; dropped probabilities are
+        // cleared in the packed fragments (element e of pf[cc] is key
+        // 32 (cc / 2) + 8 (2 (cc % 2) + e / 4) + 4 g + e % 4 of the tile) and
+        // the kept ones scaled once, in the output.
+        const int hg = a.drop.head0 + hq;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          u32x4 wv = __builtin_bit_cast(u32x4, pf[cc]);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int kb = kvb + 32 * (cc >> 1) + 8 * (2 * (cc & 1) + half) + 4 * g;
+            const uint32_t wd = drop_word(a.drop, qrow >> 2, kb >> 2, hg, qrow & 3);
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              const uint32_t lo = drop_keep_byte(wd, 2 * pr, a.drop.thr) ? 0x0000FFFFu : 0u;
+              const uint32_t hi = drop_keep_byte(wd, 2 * pr + 1, a.drop.thr) ? 0xFFFF0000u : 0u;
+              wv[2 * half + pr] &= lo | hi;
+            }
+          }
+          pf[cc] = __builtin_bit_cast(bf16x8, wv);
+        }
+      }
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
 
   l_run += shfl_xor(l_run, 32);  // both halves' sums
   if (wave_active && qrow < s) {
-    const float inv_l = 1.f / l_run;
+    const float inv_l = (DROP ? a.drop.scale : 1.f) / l_run;
     bf16* orow = a.o + (int64_t)qrow * a.ldo + (int64_t)hq * D;
 #pragma unroll
     for (int i = 0; i < ND; ++i)
@@ -318,11 +341,38 @@ __device__ __forceinline__ void seed_rows(f32x16& s, f32x16& d, float xs, float 
   ((s[R] = row_bcast<R>(xs), d[R] = row_bcast<R>(xd)), ...);
 }
 
+// Dropout in the dK/dV pass for one 32-query block: element r = 4 j + e of
+// the lane's accumulators is query 4 (q4 + 2 j) + e (q4 = (q0 + 32 qb + 4 g) / 4)
+// and key kvrow; -D of that query is broadcast from lane r of the 16-lane row
+// (xd holds -D of query n16 of the row, as for the seeds).
+template <int... J>
+__device__ __forceinline__ void drop_dkdv(f32x16& sacc, f32x16& dpacc, float xd, const DropArgs& d,
+                                          int q4, int kvrow, int hg, float sl2,
+                                          std::integer_sequence<int, J...>) {
+  auto group = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const Philox4 rw = philox4x32_10((uint32_t)(q4 + 2 * j), (uint32_t)(kvrow >> 2), (uint32_t)hg,
+                                     (uint32_t)d.batch, d.seed_lo, d.seed_hi);
+    auto elem = [&](auto ec) {
+      constexpr int e = decltype(ec)::value, r = 4 * j + e;
+      const bool keep = drop_keep_byte(rw.w[e], kvrow & 3, d.thr);
+      const float p = fast_exp2(sacc[r] * sl2);
+      sacc[r] = keep ? p : 0.f;
+      dpacc[r] = p * fmaf(keep ? d.scale : 0.f, dpacc[r], row_bcast<r>(xd));
+    };
+    elem(std::integral_constant<int, 0>());
+    elem(std::integral_constant<int, 1>());
+    elem(std::integral_constant<int, 2>());
+    elem(std::integral_constant<int, 3>());
+  };
+  (group(std::integral_constant<int, J>()), ...);
+}
+
 // ============================================================================ backward: dK, dV
 // SPLIT: the query-head-split variant (a.nparts > 1, partial sums to a.part);
 // without it the part index is a compile-time zero and nothing of the split
 // remains in the code.
-template <int D, bool SPLIT = false, bool WIN = false>
+template <int D, bool SPLIT = false, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<bf16> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
@@ -428,6 +478,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       // Seeding the accumulators with -lse (score units) and -D_i puts the row
       // statistics where the products land, with no extra registers.
       f32x16 sacc, dpacc;
+      float xd;
       {
         // Element r of a lane's accumulators is query 32 qb + 8 (r / 4) +
         // 4 g + r % 4: lane n of each 16-lane row reads the statistics of
@@ -437,8 +488,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         // eight 16-byte ones.
         const int n16 = lane & 15;
         const int qi = 32 * qb + (n16 >> 2) * 8 + 4 * g + (n16 & 3);
-        const float xl = lse_s[buf][qi], xd = dd_s[buf][qi];
-        seed_rows(sacc, dpacc, xl, xd, std::make_integer_sequence<int, 16>());
+        const float xl = lse_s[buf][qi];
+        xd = dd_s[buf][qi];
+        // with dropout the dP accumulators start at 0 and -D is added per
+        // element after the mask (dS = P (z dP~ - D))
+        seed_rows(sacc, dpacc, xl, DROP ? 0.f : xd, std::make_integer_sequence<int, 16>());
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -465,11 +519,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         }
         __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
       }
+      if constexpr (DROP) {
+        // dV takes the kept probabilities (scaled at the end); dS = P (z dP~ - D)
+        // with z = scale (kept) or 0. Element r is query q0 + 32 qb +
+        // 8 (r / 4) + 4 g + r % 4: one generator call per four queries.
+        const int hg = a.drop.head0 + hk * a.group + pp * gp + step / per_head;
+        drop_dkdv(sacc, dpacc, xd, a.drop, (q0 + 32 * qb + 4 * g) >> 2, kvrow, hg, sl2,
+                  std::make_integer_sequence<int, 4>());
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sacc[r] * sl2);
-        sacc[r] = p;
-        dpacc[r] = p * dpacc[r];
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(sacc[r] * sl2);
+          sacc[r] = p;
+          dpacc[r] = p * dpacc[r];
+        }
       }
       if (MASK && ((a.causal && kv0 + 32 * w + 31 > q0 + 32 * qb) || kv0 + 32 * w + 31 >= s ||
                    (win && q0 + 32 * qb + 31 >= kv0 + 32 * w + win))) {
@@ -531,7 +594,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         const int kv = kv0 + 32 * w + acc_row(r, g);
         if (kv < s) {
           pk[(int64_t)kv * D + d] = dkacc[i][r];
-          pv[(int64_t)kv * D + d] = dvacc[i][r];
+          pv[(int64_t)kv * D + d] = DROP ? dvacc[i][r] * a.drop.scale : dvacc[i][r];
         }
       }
     }
@@ -551,7 +614,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       }
       if (kv < s) {
         a.dk[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = (bf16)dkv;
-        a.dv[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] = (bf16)dvacc[i][r];
+        a.dv[(int64_t)kv * a.lddkv + (int64_t)hk * D + d] =
+            (bf16)(DROP ? dvacc[i][r] * a.drop.scale : dvacc[i][r]);
       }
     }
   }
@@ -590,7 +654,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnBwdArgs<bf16> a) {
 }
 
 // ============================================================================ backward: dQ
-template <int D, bool WIN = false>
+template <int D, bool WIN = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf16> a) {
   const int win = WIN ? a.window : 0;  // sliding window (compiled out when WIN is false)
   using TL = DmaTile<D>;
@@ -663,17 +727,33 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
                         (win && kvb <= q0 + 32 * w + 31 - win);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc.
+        // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc;
+        // with dropout, dS = P (z dP~ - D) with z = scale (kept) or 0.
         f32x16 sacc = zero16(), dpacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dpacc[r] = -dd_q;
+        for (int r = 0; r < 16; ++r) dpacc[r] = DROP ? 0.f : -dd_q;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
           dpacc = mma(TL::frag_at(vsa + buf * TB, rf, sb, c), df[c], dpacc);
         }
+        if constexpr (DROP) {
+          const int hg = a.drop.head0 + hq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wd = drop_word(a.drop, qrow >> 2, (kvb + 32 * sb + 8 * j + 4 * g) >> 2,
+                                          hg, qrow & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * j + e;
+              const float z = drop_keep_byte(wd, e, a.drop.thr) ? a.drop.scale : 0.f;
+              dpacc[r] = fast_exp2(fmaf(sacc[r], sl2, -lse_q)) * (z * dpacc[r] - dd_q);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+        }
         if (MASK) {
           const int qc = a.causal ? min(qrow, s - 1) : s - 1;
           const int lim = qc - kvb - 32 * sb;

@@ -113,6 +113,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ----------------------------------------------------------------- plan
 struct Plan {
   int dtype, norm, ffn, causal, rope, window;
+  int drop_thr;        // attention dropout threshold (0: none)
+  float drop_scale;
+  uint64_t seed;
   int64_t b, s, h, H, Hkv, D, f, cq, ckv, U, G, nkvc, qkv_cols, chunk_cols;
   int64_t gq;  // query blocks per weight-gradient group (backward)
   double rope_base;
@@ -155,12 +158,19 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
     return fail(BPT_EINVAL, "rope_base");
   if (!(d->norm_eps >= 0.f) || !std::isfinite(d->norm_eps)) return fail(BPT_EINVAL, "norm_eps");
   if (d->window < 0) return fail(BPT_EINVAL, "window must be >= 0");
+  if (!(d->dropout_p >= 0.f && d->dropout_p < 1.f))
+    return fail(BPT_EINVAL, "dropout_p must be in [0, 1)");
+  const int drop_thr = (int)std::lround(256.0 * (double)d->dropout_p);
+  if (drop_thr > 255) return fail(BPT_EINVAL, "dropout_p rounds to a threshold of 256");
   if (d->window > 0 && !d->causal) return fail(BPT_EINVAL, "a sliding window requires causal = 1");
   const int64_t qkv_cols = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
   if (d->seq_len * std::max<int64_t>(std::max(d->hidden, qkv_cols), d->ffn_dim) >= (int64_t(1) << 40))
     return fail(BPT_EUNSUPPORTED, "problem too large");
   p.dtype = d->dtype; p.norm = d->norm; p.ffn = d->ffn; p.causal = d->causal; p.rope = d->use_rope;
   p.window = d->window;
+  p.drop_thr = drop_thr;
+  p.drop_scale = drop_thr ? (float)(256.0 / (256.0 - drop_thr)) : 1.f;
+  p.seed = d->seed;
   p.b = d->batch; p.s = d->seq_len; p.h = d->hidden; p.H = d->n_heads; p.Hkv = d->n_kv_heads;
   p.D = d->head_dim; p.f = d->ffn_dim; p.cq = d->q_block; p.ckv = d->kv_block;
   p.U = d->head_chunk; p.G = G; p.nkvc = p.U / G; p.qkv_cols = qkv_cols;
@@ -510,10 +520,34 @@ bpt_status rope_table(hipStream_t st, const Plan& p, float2* tab) {
   return check_launch("rope_table");
 }
 
+// Calls f(window flag, dropout flag) with compile-time booleans matching the
+// plan: the sliding-window and dropout code exists only in the variants that
+// use it.
+template <class F>
+void with_variants(const Plan& p, F&& f) {
+  if (p.window) {
+    if (p.drop_thr) f(std::true_type(), std::true_type()); else f(std::true_type(), std::false_type());
+  } else {
+    if (p.drop_thr) f(std::false_type(), std::true_type()); else f(std::false_type(), std::false_type());
+  }
+}
+
+DropArgs drop_args(const Plan& p, int64_t head0, int64_t batch) {
+  DropArgs d;
+  d.seed_lo = (uint32_t)(p.seed & 0xFFFFFFFFu);
+  d.seed_hi = (uint32_t)(p.seed >> 32);
+  d.thr = p.drop_thr;
+  d.scale = p.drop_scale;
+  d.head0 = (int)head0;
+  d.batch = (int)batch;
+  return d;
+}
+
 template <typename T>
 bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v, T* o,
-                    float* lse) {
+                    float* lse, int64_t head0, int64_t batch) {
   AttnFwdArgs<T> a;
+  a.drop = drop_args(p, head0, batch);
   a.q = q; a.k = k; a.v = v; a.o = o; a.ldo = p.H * p.D; a.lse = lse;
   a.s = (int)p.s; a.nh = (int)p.U; a.group = (int)p.G; a.causal = p.causal; a.window = p.window;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
@@ -521,24 +555,25 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
   // The sliding window is a compile-time variant (WIN), so the unwindowed
   // kernels carry none of its code.
-  auto go = [&](auto winc) {
-    constexpr bool W = decltype(winc)::value;
+  auto go = [&](auto winc, auto dropc) {
+    constexpr bool W = decltype(winc)::value, R = decltype(dropc)::value;
     if constexpr (sizeof(T) == 2) {
-      if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128, W>), grid, blk, 0, st, a); return; }
-      if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64, W>), grid, blk, 0, st, a); return; }
+      if (p.D == 128) { hipLaunchKernelGGL((attn_fwd_dma_kernel<128, W, R>), grid, blk, 0, st, a); return; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_fwd_dma_kernel<64, W, R>), grid, blk, 0, st, a); return; }
     }
-    if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64, W>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((attn_fwd_kernel<T, 32, W>), grid, blk, 0, st, a);
+    if (p.D == 64) hipLaunchKernelGGL((attn_fwd_kernel<T, 64, W, R>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, 32, W, R>), grid, blk, 0, st, a);
   };
-  if (p.window) go(std::true_type()); else go(std::false_type());
+  with_variants(p, go);
   return check_launch("attn_fwd");
 }
 
 template <typename T>
 bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v,
                     const T* dout, const float* lse, const float* dvec, T* dq, T* dk, T* dv,
-                    const float2* rope, float* dkv_part) {
+                    const float2* rope, float* dkv_part, int64_t head0, int64_t batch) {
   AttnBwdArgs<T> a;
+  a.drop = drop_args(p, head0, batch);
   a.part = nullptr;
   a.nparts = 1;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.lddo = p.H * p.D; a.lse = lse; a.dvec = dvec;
@@ -552,8 +587,8 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   if (p.D == 128 && sizeof(T) != 2)
     return fail(BPT_EUNSUPPORTED, "fp32 attention backward supports head_dim <= 64");
   // The sliding window is a compile-time variant (W) of every kernel below.
-  auto dkdv_pass = [&](auto winc) {
-    constexpr bool W = decltype(winc)::value;
+  auto dkdv_pass = [&](auto winc, auto dropc) {
+    constexpr bool W = decltype(winc)::value, R = decltype(dropc)::value;
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DKDV, st);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
@@ -566,11 +601,11 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
       if (a.nparts > 1) a.part = dkv_part;
       const dim3 gsplit((unsigned)(wgs * a.nparts));
       if (a.nparts > 1) {
-        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, true, W>), gsplit, blk, 0, st, a);
-        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, true, W>), gsplit, blk, 0, st, a);
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, true, W, R>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, true, W, R>), gsplit, blk, 0, st, a);
       } else {
-        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, false, W>), gsplit, blk, 0, st, a);
-        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, false, W>), gsplit, blk, 0, st, a);
+        if (p.D == 128) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<128, false, W, R>), gsplit, blk, 0, st, a);
+        if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_dma_kernel<64, false, W, R>), gsplit, blk, 0, st, a);
       }
       done = p.D == 128 || p.D == 64;
       if (a.nparts > 1) {
@@ -580,26 +615,26 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
       }
     }
     if (!done) {
-      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64, W>), gkv, blk, 0, st, a);
-      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32, W>), gkv, blk, 0, st, a);
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64, W, R>), gkv, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 32, W, R>), gkv, blk, 0, st, a);
     }
   };
-  auto dq_pass = [&](auto winc) {
-    constexpr bool W = decltype(winc)::value;
+  auto dq_pass = [&](auto winc, auto dropc) {
+    constexpr bool W = decltype(winc)::value, R = decltype(dropc)::value;
     TimedLaunch tl(BPT_KERNEL_ATTN_BWD_DQ, st);
     bool done = false;
     if constexpr (sizeof(T) == 2) {
-      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, W>), gq, blk, 0, st, a); done = true; }
-      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<64, W>), gq, blk, 0, st, a); done = true; }
+      if (p.D == 128) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<128, W, R>), gq, blk, 0, st, a); done = true; }
+      if (p.D == 64) { hipLaunchKernelGGL((attn_bwd_dq_dma_kernel<64, W, R>), gq, blk, 0, st, a); done = true; }
     }
     if (!done) {
-      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64, W>), gq, blk, 0, st, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32, W>), gq, blk, 0, st, a);
+      if (p.D == 64) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64, W, R>), gq, blk, 0, st, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 32, W, R>), gq, blk, 0, st, a);
     }
   };
-  if (p.window) dkdv_pass(std::true_type()); else dkdv_pass(std::false_type());
+  with_variants(p, dkdv_pass);
   BPT_TRY(check_launch("attn_bwd_dkdv"));
-  if (p.window) dq_pass(std::true_type()); else dq_pass(std::false_type());
+  with_variants(p, dq_pass);
   return check_launch("attn_bwd_dq");
 }
 
@@ -676,7 +711,8 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
-      BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s));
+      BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s,
+                          ch * p.U, bi));
     }
     // Output projection + residual, Norm2 and the FFN, a group of gq
     // consecutive query blocks at a time.
@@ -850,7 +886,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       T* dK = w.dqkv + p.U * p.D;
       T* dV = w.dqkv + (p.U + p.nkvc) * p.D;
       BPT_TRY(attn_bwd<T>(st, p, w.q, w.k, w.v, w.dO + hq0 * p.D, Lb + hq0 * p.s,
-                          w.dvec + hq0 * p.s, w.dqkv, dK, dV, w.rope, w.dkv_part));
+                          w.dvec + hq0 * p.s, w.dqkv, dK, dV, w.rope, w.dkv_part, hq0, bi));
       const int64_t segc[3] = {0, p.U * p.D, (p.U + p.nkvc) * p.D};
       const int64_t wcol[3] = {hq0 * p.D, (p.H + hk0) * p.D, (p.H + p.Hkv + hk0) * p.D};
       const int64_t wid[3] = {p.U * p.D, p.nkvc * p.D, p.nkvc * p.D};

@@ -50,6 +50,8 @@ int main(void) {
          sizeof(bpt_layer_weights), sizeof(bpt_layer_grads));
   F(bpt_layer_desc, batch) F(bpt_layer_desc, head_chunk) F(bpt_layer_desc, rope_base)
   F(bpt_layer_desc, norm_eps) F(bpt_layer_grads, accumulate) F(bpt_layer_weights, n2_b)
+  F(bpt_layer_desc, window) F(bpt_layer_desc, dropout_p) F(bpt_layer_desc, seed)
+  F(bpt_stack_desc, n_layers) F(bpt_lm_head_desc, chunk_rows)
   return 0;
 }
 ''')
@@ -67,7 +69,12 @@ int main(void) {
                               "bpt_layer_desc.rope_base": (bpt.BptLayerDesc, "rope_base"),
                               "bpt_layer_desc.norm_eps": (bpt.BptLayerDesc, "norm_eps"),
                               "bpt_layer_grads.accumulate": (bpt.BptLayerGrads, "accumulate"),
-                              "bpt_layer_weights.n2_b": (bpt.BptLayerWeights, "n2_b")}.items():
+                              "bpt_layer_weights.n2_b": (bpt.BptLayerWeights, "n2_b"),
+                              "bpt_layer_desc.window": (bpt.BptLayerDesc, "window"),
+                              "bpt_layer_desc.dropout_p": (bpt.BptLayerDesc, "dropout_p"),
+                              "bpt_layer_desc.seed": (bpt.BptLayerDesc, "seed"),
+                              "bpt_stack_desc.n_layers": (bpt.BptStackDesc, "n_layers"),
+                              "bpt_lm_head_desc.chunk_rows": (bpt.BptLmHeadDesc, "chunk_rows")}.items():
         assert int(lines[key]) == getattr(cls, field).offset, key
 
 
@@ -91,13 +98,13 @@ def test_workloads_validate(name):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("abi_version", 2, 1), ("dtype", 7, 1), ("norm", 3, 1), ("ffn", 9, 1), ("causal", 2, 1),
+    ("abi_version", 1, 1), ("abi_version", 3, 1), ("dtype", 7, 1), ("norm", 3, 1), ("ffn", 9, 1), ("causal", 2, 1),
     ("seq_len", 8200, 1), ("seq_len", 0, 1), ("hidden", 2000, 1), ("n_kv_heads", 3, 1),
     ("head_dim", 96, 3), ("ffn_dim", 100, 1), ("q_block", 1000, 1), ("kv_block", 3000, 1),
     ("head_chunk", 3, 1), ("head_chunk", 0, 1), ("norm_eps", float("nan"), 1),
     # the norm kernels take rows of at most 16384 elements
     ("hidden", 32768, 3),
-    ("window", -1, 1),
+    ("window", -1, 1), ("dropout_p", 1.0, 1), ("dropout_p", -0.1, 1), ("dropout_p", 0.999, 1),
 ])
 def test_invalid_descriptors(field, value, status):
     d = _desc(**{field: value})

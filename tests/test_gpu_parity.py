@@ -198,6 +198,27 @@ def test_window_edge_cases():
         assert np.array_equal(a["grads"][k], b["grads"][k]), k
 
 
+def test_dropout_head_chunks_and_batch():
+    """Dropout masks follow the global query head and the sequence index: the
+    result does not depend on the head chunk (bit for bit in the forward),
+    and two sequences in one call match the oracle, which draws a different
+    mask for each."""
+    import memory_efficient_long_amd as bpt
+    sh = wl.SMALL["bf16-d128-dropout"].replace(name="bf16-d128-dropout-b2", batch=2,
+                                               n_heads=4, n_kv_heads=4, hidden=512,
+                                               head_chunk=4)
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    _say(f"[dropout] {sh.name} b=2 H=4")
+    base = run_gpu(inp)
+    errs = compare(base, run_oracle(inp), sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+    for hc in (1, 2):
+        out = run_gpu(inp, cfg=bpt.LayerConfig.from_shape(sh.replace(head_chunk=hc)))
+        assert np.array_equal(out["y"], base["y"]), hc
+        assert compare(out, base, sh.dtype)["dx"] < 1e-3
+
+
 # ----------------------------------------------------------------- peaked softmax
 def _base_d128(causal):
     return wl.WORKLOADS["gpt1b-s8k"].replace(

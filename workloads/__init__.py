@@ -155,6 +155,23 @@ SMALL: Dict[str, LayerShape] = {
     "f32-d64-window": WORKLOADS["gpt-tiny-fp32"].replace(
         name="f32-d64-window", seq_len=400, hidden=128, n_heads=2, n_kv_heads=2, head_dim=64,
         ffn_dim=256, q_block=200, kv_block=400, head_chunk=2, window=77),
+    # Attention dropout (masks regenerated in the backward): DMA kernels at
+    # head_dim 128, and at 64 with GQA, RoPE, a window and the split dK/dV
+    # pass; register kernels in bf16 (head_dim 32) and fp32.
+    "bf16-d128-dropout": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d128-dropout", seq_len=1040, hidden=256, n_heads=2, n_kv_heads=2,
+        head_dim=128, ffn_dim=512, q_block=520, kv_block=1040, head_chunk=2, dropout_p=0.1,
+        seed=7),
+    "bf16-d64-gqa-rope-window-dropout": WORKLOADS["llama8b-s64k"].replace(
+        name="bf16-d64-gqa-rope-window-dropout", seq_len=1040, hidden=256, n_heads=4,
+        n_kv_heads=2, head_dim=64, ffn_dim=768, q_block=520, kv_block=1040, head_chunk=2,
+        window=300, dropout_p=0.2, seed=(1 << 40) + 11),
+    "bf16-d32-dropout": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d32-dropout", seq_len=528, hidden=128, n_heads=4, n_kv_heads=4, head_dim=32,
+        ffn_dim=512, q_block=264, kv_block=528, head_chunk=2, dropout_p=0.25, seed=3),
+    "f32-d64-dropout": WORKLOADS["gpt-tiny-fp32"].replace(
+        name="f32-d64-dropout", seq_len=400, hidden=128, n_heads=2, n_kv_heads=2, head_dim=64,
+        ffn_dim=256, q_block=200, kv_block=400, head_chunk=2, dropout_p=0.3, seed=5),
     "f32-d64-gqa-rope-noncausal": WORKLOADS["gpt-tiny-fp32"].replace(
         name="f32-d64-gqa-rope-noncausal", seq_len=240, hidden=256, n_heads=4, n_kv_heads=2,
         head_dim=64, ffn_dim=512, norm="rmsnorm", ffn="gelu", causal=False,
