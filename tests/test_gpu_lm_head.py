@@ -117,6 +117,43 @@ def test_lm_head_accumulate_and_reproducible():
     assert err < 1e-6
 
 
+def test_lm_head_no_writes_outside_outputs():
+    """loss, saved, dz, dW and both workspaces, each sized exactly, between
+    guard regions that must come back untouched."""
+    import memory_efficient_long_amd as bpt
+    sh = wl.LM_HEADS["lmhead-small-bf16"]
+    _say(f"[lm-head guards] {sh.name}")
+    inp = LmInputs(sh)
+    cfg = bpt.LmHeadConfig(sh.rows, sh.hidden, sh.vocab, sh.chunk_rows, sh.dtype)
+    d = cfg.desc()
+    z, w = _dev(inp.z), _dev(inp.w)
+    t = torch.from_numpy(inp.t).cuda()
+    g = torch.from_numpy(inp.g).cuda()
+    guard = 4096
+    bufs = []
+
+    def guarded(numel, dtype, shape=None):
+        buf = torch.full((numel + 2 * guard,), 7, dtype=dtype, device="cuda")
+        bufs.append(buf)
+        v = buf[guard:guard + numel]
+        return v.view(shape) if shape is not None else v
+
+    loss = guarded(sh.rows, torch.float32)
+    saved = guarded(bpt.bpt_lm_head_saved_size(d), torch.uint8)
+    ws_f = guarded(bpt.bpt_lm_head_workspace_size(d, False), torch.uint8)
+    ws_b = guarded(bpt.bpt_lm_head_workspace_size(d, True), torch.uint8)
+    dz = guarded(z.numel(), z.dtype, z.shape)
+    dw = guarded(sh.hidden * sh.vocab, torch.float32, (sh.hidden, sh.vocab))
+    assert bpt.bpt_lm_head_forward(d, z, w, t, loss, saved, ws_f) == 0
+    assert bpt.bpt_lm_head_backward(d, z, w, t, saved, g, dz, dw, ws_b, False) == 0
+    torch.cuda.synchronize()
+    for buf in bufs:
+        assert torch.all(buf[:guard] == 7) and torch.all(buf[-guard:] == 7)
+    ref = _run_gpu(inp)
+    assert torch.equal(loss, ref["loss"]) and torch.equal(dz, ref["dz"])
+    assert torch.equal(dw, ref["dw"])
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_lm_head_full_size_sampled_rows():

@@ -88,38 +88,50 @@ def test_block_size_and_head_chunk_invariance():
                            sh.dtype)["d" + k] < 1e-3, k
 
 
-def test_no_writes_outside_outputs_and_reproducible():
+@pytest.mark.parametrize("name", ["llama8b-small", "bf16-d64-gqa-rope-window-dropout",
+                                  "f32-d64-window"])
+def test_no_writes_outside_outputs_and_reproducible(name):
+    """Every buffer the library writes (y, saved, dx, each gradient and both
+    workspaces, each sized exactly) sits between guard regions that must come
+    back untouched; a second forward and backward reproduce every bit."""
     import memory_efficient_long_amd as bpt
     from harness import to_device
-    sh = wl.SMALL["llama8b-small"]
-    inp = Inputs(sh, norm_std=0.2)
+    sh = wl.SMALL[name]
+    _say(f"[guards] {name}")
+    inp = Inputs(sh, bias_std=0.2 if sh.has_bias else 0.0, norm_std=0.2)
     cfg = bpt.LayerConfig.from_shape(sh)
+    d = cfg.desc()
     x = to_device(inp.x)
     w = {k: to_device(v) for k, v in inp.w.items()}
     dy = to_device(inp.dy)
     guard = 4096
+    bufs = []
+
+    def guarded(numel, dtype, shape=None):
+        buf = torch.full((numel + 2 * guard,), 7, dtype=dtype, device="cuda")
+        bufs.append(buf)
+        t = buf[guard:guard + numel]
+        return t.view(shape) if shape is not None else t
+
     n = x.numel()
-    ybuf = torch.full((n + 2 * guard,), 7.0, dtype=x.dtype, device="cuda")
-    dxbuf = torch.full((n + 2 * guard,), 7.0, dtype=x.dtype, device="cuda")
-    y = ybuf[guard:guard + n].view_as(x)
-    dx = dxbuf[guard:guard + n].view_as(x)
-    grads = {}
-    gbufs = {}
-    for k, shp in bpt.grad_shapes(cfg, w).items():
-        numel = int(np.prod(shp))
-        gbufs[k] = torch.full((numel + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
-        grads[k] = gbufs[k][guard:guard + numel].view(shp)
-    y1, saved = bpt.forward(cfg, x, w, y=y)
-    bpt.backward(cfg, x, w, saved, dy, dx=dx, grads=grads)
+    y = guarded(n, x.dtype, x.shape)
+    dx = guarded(n, x.dtype, x.shape)
+    saved = guarded(bpt.bpt_layer_saved_size(d), torch.uint8)
+    ws_f = guarded(bpt.bpt_layer_workspace_size(d, False), torch.uint8)
+    ws_b = guarded(bpt.bpt_layer_workspace_size(d, True), torch.uint8)
+    grads = {k: guarded(int(np.prod(shp)), torch.float32, shp)
+             for k, shp in bpt.grad_shapes(cfg, w).items()}
+    y1, _ = bpt.forward(cfg, x, w, y=y, saved=saved, workspace=ws_f)
+    bpt.backward(cfg, x, w, saved, dy, dx=dx, grads=grads, workspace=ws_b)
     y2, saved2 = bpt.forward(cfg, x, w)
     # A second backward into fresh buffers: the same bits (no atomics; split
     # sums are reduced in a fixed order).
     dx2, grads2 = bpt.backward(cfg, x, w, saved2, dy)
     torch.cuda.synchronize()
-    for buf in [ybuf, dxbuf, *gbufs.values()]:
-        assert torch.all(buf[:guard] == 7.0) and torch.all(buf[-guard:] == 7.0)
+    for buf in bufs:
+        assert torch.all(buf[:guard] == 7) and torch.all(buf[-guard:] == 7)
     assert torch.equal(y1, y2)
-    assert torch.equal(saved, saved2)
+    assert torch.equal(saved, saved2[:saved.numel()])
     assert torch.equal(dx, dx2)
     for k in grads:
         assert torch.equal(grads[k], grads2[k]), k
