@@ -82,6 +82,71 @@ __device__ __forceinline__ bool drop_keep_byte(uint32_t word, int byte, int thr)
   return (int)((word >> (8 * byte)) & 0xFFu) >= thr;
 }
 
+// ---- Sharing one generator call among the four lanes that need it.
+// In the head_dim 64/128 kernels the four lanes of a quad (lanes 4k .. 4k+3)
+// own four consecutive queries (or keys) of one 4 x 4 block row (column), so
+// they need the same calls. Each lane computes a different one and a 4 x 4
+// transpose across the quad redistributes the words: a quarter of the calls.
+
+// Lane value from lane (quad_base + PERM[lane % 4]) (DPP quad_perm).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// 4 x 4 transpose of words across a quad: afterwards lane i holds in a[j] what
+// lane j held in a[i]. Two exchange stages (partner lane ^ 1, then ^ 2); in
+// each, a lane keeps the two words whose index matches its own lane bit and
+// takes the partner's other two.
+__device__ __forceinline__ void quad_transpose(uint32_t (&a)[4], int lane) {
+  const bool odd = lane & 1, hi = lane & 2;
+  {
+    const uint32_t s0 = odd ? a[0] : a[1], s1 = odd ? a[2] : a[3];
+    const uint32_t r0 = quad_perm<0xB1>(s0), r1 = quad_perm<0xB1>(s1);  // [1, 0, 3, 2]
+    a[0] = odd ? r0 : a[0];
+    a[1] = odd ? a[1] : r0;
+    a[2] = odd ? r1 : a[2];
+    a[3] = odd ? a[3] : r1;
+  }
+  {
+    const uint32_t s0 = hi ? a[0] : a[2], s1 = hi ? a[1] : a[3];
+    const uint32_t r0 = quad_perm<0x4E>(s0), r1 = quad_perm<0x4E>(s1);  // [2, 3, 0, 1]
+    a[0] = hi ? r0 : a[0];
+    a[1] = hi ? r1 : a[1];
+    a[2] = hi ? a[2] : r0;
+    a[3] = hi ? a[3] : r1;
+  }
+}
+
+// Query-row lanes: lane i of a quad (its query q has q % 4 = i) computes the
+// call for key group k4[i] and returns, in w[j], word i of the call for key
+// group k4[j] -- the four keys of group k4[j] for its own query.
+__device__ __forceinline__ void drop_words_rows(const DropArgs& d, int q4, int my_k4, int hg,
+                                                int lane, uint32_t (&w)[4]) {
+  const Philox4 c = philox4x32_10((uint32_t)q4, (uint32_t)my_k4, (uint32_t)hg, (uint32_t)d.batch,
+                                  d.seed_lo, d.seed_hi);
+  w[0] = c.w[0]; w[1] = c.w[1]; w[2] = c.w[2]; w[3] = c.w[3];
+  quad_transpose(w, lane);
+}
+
+// Key-row lanes: lane i of a quad (its key k has k % 4 = i) computes the call
+// for query group q4[i]; returns in b[j] the four bytes i of the words of the
+// call for query group q4[j] (byte e: query 4 q4[j] + e with this lane's key).
+__device__ __forceinline__ void drop_bytes_cols(const DropArgs& d, int my_q4, int k4, int hg,
+                                                int lane, uint32_t (&b)[4]) {
+  const Philox4 c = philox4x32_10((uint32_t)my_q4, (uint32_t)k4, (uint32_t)hg, (uint32_t)d.batch,
+                                  d.seed_lo, d.seed_hi);
+  // byte transpose inside the lane: b[t] = byte t of words 0, 1, 2, 3
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t sel = (uint32_t)t | ((uint32_t)(4 + t) << 8) | 0x0C0C0000u;
+    const uint32_t x01 = __builtin_amdgcn_perm(c.w[1], c.w[0], sel);
+    const uint32_t x23 = __builtin_amdgcn_perm(c.w[3], c.w[2], sel);
+    b[t] = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+  }
+  quad_transpose(b, lane);
+}
+
 template <typename T>
 struct AttnFwdArgs {
   const T* q; const T* k; const T* v;  // head-major: q [nh, s, D], k/v [nkv, s, D]

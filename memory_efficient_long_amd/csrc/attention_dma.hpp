@@ -281,14 +281,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
         // cleared in the packed fragments (element e of pf[cc] is key
         // 32 (cc / 2) + 8 (2 (cc % 2) + e / 4) + 4 g + e % 4 of the tile) and
         // the kept ones scaled once, in the output.
+        // Key group (4 keys) kvb / 4 + 2 m + g for m = 2 cc + half; the calls
+        // for m = 4 rd + j are shared by the quad (lane j computes it).
         const int hg = a.drop.head0 + hq;
+        uint32_t wds[2][4];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+          drop_words_rows(a.drop, qrow >> 2, (kvb >> 2) + 2 * (4 * rd + (lane & 3)) + g, hg, lane,
+                          wds[rd]);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           u32x4 wv = __builtin_bit_cast(u32x4, pf[cc]);
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int kb = kvb + 32 * (cc >> 1) + 8 * (2 * (cc & 1) + half) + 4 * g;
-            const uint32_t wd = drop_word(a.drop, qrow >> 2, kb >> 2, hg, qrow & 3);
+            const int m = 2 * cc + half;
+            const uint32_t wd = wds[m >> 2][m & 3];
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
               const uint32_t lo = drop_keep_byte(wd, 2 * pr, a.drop.thr) ? 0x0000FFFFu : 0u;
@@ -349,13 +356,15 @@ template <int... J>
 __device__ __forceinline__ void drop_dkdv(f32x16& sacc, f32x16& dpacc, float xd, const DropArgs& d,
                                           int q4, int kvrow, int hg, float sl2,
                                           std::integer_sequence<int, J...>) {
+  // the four query groups' calls are shared by the quad (lane i computes
+  // group q4 + 2 i); bq[j] holds this key's byte of each word of group j
+  uint32_t bq[4];
+  drop_bytes_cols(d, q4 + 2 * (kvrow & 3), kvrow >> 2, hg, kvrow, bq);  // kvrow % 4 = lane % 4
   auto group = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    const Philox4 rw = philox4x32_10((uint32_t)(q4 + 2 * j), (uint32_t)(kvrow >> 2), (uint32_t)hg,
-                                     (uint32_t)d.batch, d.seed_lo, d.seed_hi);
     auto elem = [&](auto ec) {
       constexpr int e = decltype(ec)::value, r = 4 * j + e;
-      const bool keep = drop_keep_byte(rw.w[e], kvrow & 3, d.thr);
+      const bool keep = drop_keep_byte(bq[j], e, d.thr);
       const float p = fast_exp2(sacc[r] * sl2);
       sacc[r] = keep ? p : 0.f;
       dpacc[r] = p * fmaf(keep ? d.scale : 0.f, dpacc[r], row_bcast<r>(xd));
@@ -739,10 +748,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
         }
         if constexpr (DROP) {
           const int hg = a.drop.head0 + hq;
+          // key group (kvb + 32 sb + 8 j + 4 g) / 4, shared by the quad
+          uint32_t wds[4];
+          drop_words_rows(a.drop, qrow >> 2, ((kvb + 32 * sb + 4 * g) >> 2) + 2 * (lane & 3), hg,
+                          lane, wds);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t wd = drop_word(a.drop, qrow >> 2, (kvb + 32 * sb + 8 * j + 4 * g) >> 2,
-                                          hg, qrow & 3);
+            const uint32_t wd = wds[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * j + e;
