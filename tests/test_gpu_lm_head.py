@@ -97,6 +97,31 @@ def test_lm_head_matches_oracle(name, w_scale):
     assert np.all(to_host64(gpu["dz"])[ign] == 0.0)
 
 
+@pytest.mark.parametrize("case", ["one-tile", "all-ignored"])
+def test_lm_head_degenerate(case):
+    """Fewer rows than one tile with the smallest vocabulary (one column
+    tile), and a chunk whose every target is ignored (zero loss and dz)."""
+    from oracle import lm_head_oracle as lmo
+    base = wl.LM_HEADS["lmhead-small-bf16"]
+    if case == "one-tile":
+        sh = base.replace(name="lmhead-one-tile", rows=37, hidden=64, vocab=64, chunk_rows=64,
+                          ignore_every=0)
+    else:
+        sh = base.replace(name="lmhead-all-ignored", rows=200, chunk_rows=64, ignore_every=1)
+    _say(f"[lm-head] {sh.name} rows={sh.rows} h={sh.hidden} V={sh.vocab}")
+    inp = LmInputs(sh)
+    gpu = _run_gpu(inp)
+    ref = lmo.lm_head_ce(inp.z.f64(), inp.w.f64(), inp.t, inp.g.astype(np.float64))
+    if case == "all-ignored":
+        assert np.all(to_host64(gpu["loss"]) == 0.0) and np.all(to_host64(gpu["dz"]) == 0.0)
+        assert np.all(to_host64(gpu["dw"]) == 0.0)
+        return
+    errs = _errs(gpu, ref)
+    _say(f"  errs {errs}")
+    bad = over_bar(errs, sh.dtype)
+    assert not bad, bad
+
+
 def test_lm_head_accumulate_and_reproducible():
     import memory_efficient_long_amd as bpt
     sh = wl.LM_HEADS["lmhead-small-bf16"]

@@ -210,6 +210,37 @@ def test_window_edge_cases():
         assert np.array_equal(a["grads"][k], b["grads"][k]), k
 
 
+DEGENERATE = {
+    # the shortest sequence (one partial tile of every kernel), both precisions
+    "min-seq-bf16-d128": wl.SMALL["gpt1b-small"].replace(
+        name="min-seq-bf16-d128", seq_len=16, q_block=16, kv_block=16, ffn_dim=256),
+    "min-seq-f32-d32": wl.SMALL["gpt-tiny-fp32"].replace(
+        name="min-seq-f32-d32", seq_len=16, q_block=8, kv_block=16, ffn_dim=64),
+    # one KV head for all query heads (the dK/dV pass splits the group)
+    "mqa-bf16-d128-rope": wl.SMALL["llama8b-small"].replace(
+        name="mqa-bf16-d128-rope", seq_len=272, n_kv_heads=1, q_block=136, kv_block=272,
+        head_chunk=4, ffn_dim=512),
+    # several sequences with GQA and RoPE, a ragged length
+    "batch3-bf16-d64-gqa-rope": wl.SMALL["bf16-d64-gqa-rope"].replace(
+        name="batch3-bf16-d64-gqa-rope", batch=3, seq_len=176, q_block=88, kv_block=176),
+    # one query block per sequence, key blocks of one row
+    "one-block-bf16-d64": wl.SMALL["bf16-d64-noncausal"].replace(
+        name="one-block-bf16-d64", causal=True, seq_len=336, q_block=336, kv_block=1),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_degenerate_shapes_match_oracle(name):
+    sh = DEGENERATE[name]
+    _say(f"[degenerate] {name} b={sh.batch} s={sh.seq_len} H={sh.n_heads}/{sh.n_kv_heads} "
+         f"d={sh.head_dim} {sh.dtype}")
+    inp = Inputs(sh, bias_std=0.2 if sh.has_bias else 0.0, norm_std=0.2)
+    errs = compare(run_gpu(inp), run_oracle(inp), sh.dtype, residual_x=inp.x.f64(),
+                   dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+
+
 def test_dropout_head_chunks_and_batch():
     """Dropout masks follow the global query head and the sequence index: the
     result does not depend on the head chunk (bit for bit in the forward),
