@@ -436,6 +436,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const int qt1 = win ? min(nqt, (kv0 + BKV + win - 2) / BQ + 1) : nqt;
   const int per_head = qt1 - qt0;
   const int nsteps = per_head * gp;
+  // Query tiles are visited from the last one down: the workgroups resident
+  // on an XCD (consecutive key tiles of one head) then start on the same tile
+  // and sweep the head's Q and dO together through that XCD's L2, instead of
+  // starting two tiles apart each (a spread that outgrows the L2 along the way).
+  auto q_tile = [&](int step) { return qt1 - 1 - step % per_head; };
 
   // Row statistics of the next step: loaded raw (before the tile loads, so
   // waiting for them never waits for the tiles) and converted when stored.
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   const typename TL::template Loader<BQ, 4> qld(D, lane), dold(a.lddo, lane);
   auto load_step = [&](int step, int buf) {
     const int hq = hk * a.group + pp * gp + step / per_head;
-    const int q0 = (qt0 + step % per_head) * BQ;
+    const int q0 = q_tile(step) * BQ;
     if (tid < BQ) {
       const int qr = q0 + tid;
       valid_r = qr < s;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
   // stay next to their reads instead of occupying a register each.
   auto q_step = [&](int step, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int q0 = (qt0 + step % per_head) * BQ;
+    const int q0 = q_tile(step) * BQ;
     asm volatile("" : "+v"(rf), "+v"(trb));
     if (step + 1 < nsteps) load_step(step + 1, buf ^ 1);
     const bool MASK = (a.causal && kv0 + BKV - 1 > q0) || kv0 + BKV - 1 >= s ||
