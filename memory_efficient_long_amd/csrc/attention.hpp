@@ -88,10 +88,11 @@ __device__ __forceinline__ bool drop_keep_byte(uint32_t word, int byte, int thr)
 // they need the same calls. Each lane computes a different one and a 4 x 4
 // transpose across the quad redistributes the words: a quarter of the calls.
 
-// Lane value from lane (quad_base + PERM[lane % 4]) (DPP quad_perm).
+// Lane value from lane (quad_base + PERM[lane % 4]) (DPP quad_perm; every
+// source lane is valid, so the move keeps no old value).
 template <int CTRL>
 __device__ __forceinline__ uint32_t quad_perm(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 
 // 4 x 4 transpose of words across a quad: afterwards lane i holds in a[j] what

@@ -336,11 +336,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   }
 }
 
-// Value of lane R of this lane's 16-lane row (DPP row_newbcast).
+// Value of lane R of this lane's 16-lane row (DPP row_newbcast). Every source
+// lane is valid, so the move keeps no old value: without bound_ctrl the
+// compiler first initialises each destination with a separate move.
 template <int R>
 __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + R, 0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + R, 0xF, 0xF, true));
 }
 template <int... R>
 __device__ __forceinline__ void seed_rows(f32x16& s, f32x16& d, float xs, float xd,

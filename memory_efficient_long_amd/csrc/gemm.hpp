@@ -60,10 +60,11 @@ __device__ __forceinline__ float sigmoidf_(float a) {
 enum ActKind { ACT_RELU = 0, ACT_GELU = 1 };
 
 // Value of lane ^ 1 (the neighbouring accumulator column): a DPP quad
-// permutation [1, 0, 3, 2], a single VALU move.
+// permutation [1, 0, 3, 2], a single VALU move (every source lane is valid,
+// so no old value is kept: no extra move to initialise the destination).
 __device__ __forceinline__ float lane_xor1(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 
 // ----------------------------------------------------------------- epilogues
