@@ -105,15 +105,19 @@ def cmd_counters(args) -> None:
     per = {}  # kernel -> counter -> {dispatch: value}
     for path in args.csv:
         for r in csv.DictReader(open(path)):
-            name = short_name(r["Kernel_Name"])
-            if not re.search(args.kernels, name):
+            if not re.search(args.kernels, r["Kernel_Name"]):
                 continue
+            name = args.aggregate or short_name(r["Kernel_Name"])
             d = per.setdefault(name, {}).setdefault(r["Counter_Name"], {})
             d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     names = sorted({c for k in per.values() for c in k})
-    med = {k: {c: statistics.median(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+    reduce = (lambda v: sum(v)) if args.aggregate else statistics.median
+    med = {k: {c: reduce(list(v.values())) for c, v in cs.items()} for k, cs in per.items()}
+    how = (f"Totals over all {max(len(v) for cs in per.values() for v in cs.values())} matching "
+           "dispatches of one step." if args.aggregate else
+           "Medians over the dispatches of each kernel (counter totals per dispatch).")
     lines = [f"# rocprofv3 counters: {args.title}", "", f"Command: `{args.cmd}`", "",
-             "Medians over the dispatches of each kernel (counter totals per dispatch).", "",
+             how, "",
              "| counter | " + " | ".join(f"`{k}`" for k in med) + " |",
              "|---|" + "---|" * len(med)]
     for c in names:
@@ -156,7 +160,9 @@ def main() -> None:
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
     c.add_argument("--out", required=True)
-    c.add_argument("--kernels", default="attn_")
+    c.add_argument("--kernels", default="attn_", help="regular expression on kernel names")
+    c.add_argument("--aggregate", default="",
+                   help="sum every matching dispatch into one column of this name")
     c.add_argument("--cmd", default="")
     c.add_argument("--title", default="")
     args = ap.parse_args()
