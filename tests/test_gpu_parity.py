@@ -399,6 +399,26 @@ def test_dense_long_sequence_window():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
+def test_dense_long_sequence_dropout():
+    """Attention dropout at s = 4096 with GQA (4 query heads on 2 KV heads,
+    head_dim 128), dense cotangent: the mask counters run over 1024 query
+    and key groups per head, and the dK/dV pass takes its query-head split
+    with dropout."""
+    sh = wl.WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-d128-s4k-gqa-dropout", seq_len=4096, hidden=512, n_heads=4, n_kv_heads=2,
+        head_dim=128, ffn_dim=512, q_block=1024, kv_block=2048, head_chunk=4, dropout_p=0.1,
+        seed=12345)
+    _say(f"[dense-dropout] s={sh.seq_len} p={sh.dropout_p} H={sh.n_heads}/{sh.n_kv_heads}")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    gpu = run_gpu(inp)
+    ref = run_oracle(inp)
+    errs = compare(gpu, ref, sh.dtype, residual_x=inp.x.f64(), dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_full_size_dense_gpt1b_s8k():
     """The GPT-1B-shaped layer at s = 8192 exactly as specified, with a dense
     cotangent over every row."""
