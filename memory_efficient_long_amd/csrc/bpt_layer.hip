@@ -353,10 +353,13 @@ bpt_status launch_gemm_dma(hipStream_t st, const bf16* A, int64_t lda, const bf1
 }
 
 // kbuf (kbuf_floats fp32 elements of workspace), when given, lets a weight
-// gradient with a long reduction (K >= 16384, the sequence) and too few output
-// tiles to fill the GPU run split-K: ksplit copies of the tile grid each sum
-// K / ksplit steps into kbuf, and a second kernel applies the epilogue to
-// their sum.
+// gradient with too few output tiles to fill the GPU run split-K: ksplit
+// copies of the tile grid each sum a share of the reduction steps into kbuf,
+// and a second kernel applies the epilogue to their sum (in a fixed order).
+// Long reductions (K >= 16384, the sequence) use 256 x 256 tiles and shares
+// of at least 2048; smaller outputs (fewer 256 x 256 tiles than CUs, e.g. the
+// per-group FFN weight gradients of a narrow layer) 128 x 128 tiles and
+// shares of at least two steps.
 template <typename T, bool AK, bool BK, class Epi>
 bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb, int64_t M,
                 int64_t N, int64_t K, const Epi& epi, const char* what, float* kbuf = nullptr,
@@ -390,6 +393,19 @@ bpt_status gemm(hipStream_t st, const T* A, int64_t lda, const T* B, int64_t ldb
             EpiPart ep{kbuf, N, M * N};
             BPT_TRY((launch_gemm_dma<AK, BK, 256, 256, 64, 2, 128, 64, 8>(st, A, lda, B, ldb, M, N,
                                                                           K, ep, ks)));
+            hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((M * N + 255) / 256)),
+                               dim3(256), 0, st, kbuf, ks, (int)M, (int)N, epi);
+            return check_launch(what);
+          }
+        } else if (kbuf && K >= 1024 && nt256 < device_cus()) {
+          const int64_t nt128 = ((M + 127) / 128) * ((N + 127) / 128), nkt = K / 64;
+          int ks = 1;
+          while (nt128 * ks < 2 * device_cus() && ks < 64 && nkt / (2 * ks) >= 2) ks *= 2;
+          while (ks > 1 && ks * M * N > kbuf_floats) ks /= 2;
+          if (ks > 1) {
+            EpiPart ep{kbuf, N, M * N};
+            BPT_TRY((launch_gemm_dma<AK, BK, 128, 128, 64, 2, 32, 64, 8>(st, A, lda, B, ldb, M, N,
+                                                                        K, ep, ks)));
             hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((M * N + 255) / 256)),
                                dim3(256), 0, st, kbuf, ks, (int)M, (int)N, epi);
             return check_launch(what);
@@ -844,15 +860,18 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
       // Weight gradients of the group, reduced over all of its rows.
       if (dw2) {
         EpiOut<T, float> e{dw2, p.h, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyg, p.h, p.f, p.h, rows, e, "dW2")));
+        BPT_TRY((gemm<T, false, false>(st, w.u, p.f, dyg, p.h, p.f, p.h, rows, e, "dW2", w.kbuf,
+                                       w.kbuf_floats)));
       }
       if (dw1) {
         EpiOut<T, float> e{dw1, p.f, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, rows, e, "dW1")));
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.da, p.f, p.h, p.f, rows, e, "dW1", w.kbuf,
+                                       w.kbuf_floats)));
       }
       if (dw3) {
         EpiOut<T, float> e{dw3, p.f, nullptr, 1.f, 1};
-        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, rows, e, "dW3")));
+        BPT_TRY((gemm<T, false, false>(st, w.z, p.h, w.dup, p.f, p.h, p.f, rows, e, "dW3", w.kbuf,
+                                       w.kbuf_floats)));
       }
     }
     // ---- O-projection backward over the whole sequence: dW_o += O^T dh,

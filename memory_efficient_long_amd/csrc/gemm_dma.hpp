@@ -183,7 +183,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int nt = tiles_m * tiles_n;
   // Split-K: the grid holds ksplit copies of the tile grid, copy k summing
-  // reduction steps [k K / ksplit, (k + 1) K / ksplit) (host: K % (ksplit BK) == 0).
+  // the reduction steps [k n / ksplit, (k + 1) n / ksplit) of the n = K / BK
+  // steps (host: K % BK == 0, ksplit <= n).
   const int split = blockIdx.x / nt;
   int tile;
   {
@@ -209,7 +210,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = zero16();
 
-  const int nk = K / ksplit / BK, kbase = split * nk * BK;
+  const int nkt = K / BK;
+  const int k0s = (int)((int64_t)split * nkt / ksplit);
+  const int nk = (int)((int64_t)(split + 1) * nkt / ksplit) - k0s, kbase = k0s * BK;
   const typename OA::template Loader<NW> la(A, lda, m0, M, w, lane);
   const typename OB::template Loader<NW> lb(B, ldb, n0, N, w, lane);
   auto issue = [&](int kt) {
