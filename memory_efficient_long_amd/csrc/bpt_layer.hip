@@ -274,8 +274,8 @@ BwdWs<T> carve_bwd(Carver& c, const Plan& p) {
   w.part = c.take<float>(kColsumParts * maxn);
   w.npart_g = c.take<float>(kNormWaves * p.h);
   w.npart_b = c.take<float>(kNormWaves * p.h);
-  // Split-K partial sums of the sequence-long weight-gradient GEMMs (bf16
-  // path): s h / 4 floats, one byte per token and hidden unit.
+  // Split-K partial sums of the weight-gradient GEMMs whose outputs have few
+  // tiles (bf16 path): s h / 4 floats, one byte per token and hidden unit.
   w.kbuf_floats = p.dtype == BPT_BF16 ? p.s * p.h / 4 : 0;
   w.kbuf = w.kbuf_floats ? c.take<float>(w.kbuf_floats) : nullptr;
   // Partial dK/dV sums of the query-head split (bf16, GQA with fewer than 8
