@@ -397,6 +397,20 @@ def test_dense_long_sequence_window():
     _check(errs, sh.dtype)
 
 
+def test_narrow_layer_uneven_split_k():
+    """One layer of the RL small-hidden shape (h = 128, one head of 128,
+    FFN 512) at s = 16000, dense cotangent: its per-group FFN weight
+    gradients (groups of 8000 rows = 125 reduction steps, 2 x 4 output
+    tiles) run split-K in uneven shares of 3 and 4 steps."""
+    sh = wl.RL_SMALL_H.replace(name="rl-layer-s16k", seq_len=16000)
+    _say(f"[narrow] {sh.name} s={sh.seq_len} h={sh.hidden}")
+    inp = Inputs(sh, bias_std=0.2, norm_std=0.2)
+    errs = compare(run_gpu(inp), run_oracle(inp), sh.dtype, residual_x=inp.x.f64(),
+                   dy=inp.dy.f64())
+    _say(f"  errs {_fmt(errs)}")
+    _check(errs, sh.dtype)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_dense_long_sequence_dropout():
