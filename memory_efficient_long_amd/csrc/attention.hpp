@@ -20,13 +20,18 @@
 //  * dK/dV pass: a workgroup owns 128 key rows of one KV head (32 per wave,
 //    held in registers) and walks the query tiles at or after its diagonal for
 //    every query head of its GQA group; per 64-row query tile it rebuilds
-//    P = exp2(S log2(e)/sqrt(d) - lse), dP = dO V^T, dS = P (dP - D) with
+//    P = exp2(S - lse), dP = dO V^T, dS = P (dP - D) with
 //    D = rowsum(dO * O), and accumulates dV += P^T dO, dK += dS^T Q.
 //  * dQ pass: a workgroup owns 128 query rows (32 per wave, Q and dO in
 //    registers) and streams key/value tiles like the forward, rebuilding P and
 //    dS per tile (lane-local row terms) and accumulating dQ^T += K^T dS^T.
-// Neither pass needs atomics; the inverse RoPE rotation and the 1/sqrt(d)
-// factor are applied when dQ and dK are written.
+// Neither pass needs atomics; the inverse RoPE rotation and the scale factor
+// are applied when dQ and dK are written.
+//
+// Q arrives multiplied by log2(e)/sqrt(d) (the projection's epilogue applies
+// it before rounding), so S = Q K^T is already the scaled score in base-2
+// units and no kernel scales scores element by element; dK = dS^T q / sqrt(d)
+// becomes ln(2) dS^T Q.
 #pragma once
 
 #include <type_traits>
@@ -150,12 +155,11 @@ __device__ __forceinline__ void drop_bytes_cols(const DropArgs& d, int my_q4, in
 
 template <typename T>
 struct AttnFwdArgs {
-  const T* q; const T* k; const T* v;  // head-major: q [nh, s, D], k/v [nkv, s, D]
+  const T* q; const T* k; const T* v;  // head-major: q [nh, s, D] (times log2(e)/sqrt(D)), k/v [nkv, s, D]
   T* o; int64_t ldo;                    // token-major; head hq at column hq * D
   float* lse;                           // [nh, s], base 2
   int s, nh, group, causal;
   int window;                           // causal sliding window W (0: none): keys i - W < j <= i
-  float scale_log2;                     // log2(e) / sqrt(D)
   DropArgs drop;                        // attention dropout (used by the DROP variants)
 };
 
@@ -169,7 +173,7 @@ struct AttnBwdArgs {
   const float2* rope;                   // cos/sin [s, D/2] or null
   int s, nh, nkv, group, causal;
   int window;                           // as in AttnFwdArgs
-  float scale_log2, scale;              // log2(e)/sqrt(D), 1/sqrt(D)
+  float scale, dk_scale;                // dQ factor 1/sqrt(D); dK factor ln(2) (Q carries log2(e)/sqrt(D))
   DropArgs drop;                        // attention dropout (used by the DROP variants)
   // dK/dV split over the query heads of a KV head (bf16 head_dim 64/128):
   // nparts > 1 runs nparts workgroups per key tile, each over group / nparts
@@ -325,7 +329,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) oacc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
 
   if (ntiles > t_lo) {
     kt.load(Kp, D, t_lo * BKV, s, tid);
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * sl2;
+      mx = fmaxf(mx, shfl_xor(mx, 32));
       // Move the running max only when this tile exceeds it by > 8 (log2 units).
       if (__any(mx > m_run + 8.f)) {
         const float m_new = fmaxf(m_run, mx);
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnFwdArgs<T> a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[sb][r], sl2, -m_sub));
+          const float p = fast_exp2(sacc[sb][r] - m_sub);
           sacc[sb][r] = p;
           rs += p;
         }
@@ -485,7 +488,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) { dkacc[i] = zero16(); dvacc[i] = zero16(); }
 
-  const float sl2 = a.scale_log2;
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
   // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j + e;
             const bool keep = drop_keep_byte(rw.w[e], kvrow & 3, a.drop.thr);
-            const float p = fast_exp2(fmaf(sacc[r], sl2, -l4[j][e]));
+            const float p = fast_exp2(sacc[r] - l4[j][e]);
             sacc[r] = keep ? p : 0.f;
             dpacc[r] = p * ((keep ? a.drop.scale : 0.f) * dpacc[r] - d4[j][e]);
           }
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], sl2, -l4[r >> 2][r & 3]));
+          const float p = fast_exp2(sacc[r] - l4[r >> 2][r & 3]);
           sacc[r] = p;
           dpacc[r] = p * (dpacc[r] - d4[r >> 2][r & 3]);
         }
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs<T> a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kv = kv0 + 32 * w + acc_row(r, g);
-      float dkv = dkacc[i][r] * a.scale;
+      float dkv = dkacc[i][r] * a.dk_scale;
       const float pair = shfl_xor(dkv, 1);
       if (a.rope && kv < s) {
         const float2 cs = a.rope[(int64_t)kv * (D / 2) + (d >> 1)];
@@ -677,7 +679,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
   const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
   const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
-  const float sl2 = a.scale_log2;
 
   RowTile<T, BKV, D> ktile, vtile;
   f32x16 dqacc[ND];
@@ -720,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * j + e;
-              const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+              const float p = fast_exp2(sacc[r] - lse_q);
               const float z = drop_keep_byte(wd, e, a.drop.thr) ? a.drop.scale : 0.f;
               dpacc[r] = p * (z * dpacc[r] - dd_q);
             }
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs<T> a) {
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+            const float p = fast_exp2(sacc[r] - lse_q);
             dpacc[r] = p * (dpacc[r] - dd_q);
           }
         }

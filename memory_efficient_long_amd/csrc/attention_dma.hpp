@@ -189,8 +189,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
   f32x16 oacc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) oacc[i] = zero16();
+  // Q carries log2(e)/sqrt(D): the products are base-2 scores, and P is
+  // exp2(S - m) with no per-element scaling. (Seeding the S accumulators
+  // with -m, which would save the subtraction too, costs 16 registers that
+  // this kernel does not have: it measured slower.)
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
 
   const uint32_t ksa = lds_addr(&ks[0][0]), vsa = lds_addr(&vs[0][0]);
   const uint32_t rf = TL::rf_base(lane), trb = TL::tr_base(lane);
@@ -242,7 +245,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-      mx *= sl2;
       if (__any(mx > m_run + 8.f)) {  // move the running max only by > 2^8
         const float m_new = fmaxf(m_run, fmaxf(mx, shfl_xor(mx, 32)));
         // The branch is wave-wide: with a window, a row may still have seen no
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(fmaf(sacc[sb][r], sl2, -m_sub));
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = fast_exp2(sacc[sb][r] - m_sub);
       // P in bf16 (the B operand of O^T += V^T P^T); the row sum is taken
       // over the same bf16 values, two per dot-product instruction, so the
       // normaliser matches what the MFMAs accumulate.
@@ -356,7 +358,7 @@ __device__ __forceinline__ void seed_rows(f32x16& s, f32x16& d, float xs, float 
 // (xd holds -D of query n16 of the row, as for the seeds).
 template <int... J>
 __device__ __forceinline__ void drop_dkdv(f32x16& sacc, f32x16& dpacc, float xd, const DropArgs& d,
-                                          int q4, int kvrow, int hg, float sl2,
+                                          int q4, int kvrow, int hg,
                                           std::integer_sequence<int, J...>) {
   // the four query groups' calls are shared by the quad (lane i computes
   // group q4 + 2 i); bq[j] holds this key's byte of each word of group j
@@ -367,7 +369,7 @@ __device__ __forceinline__ void drop_dkdv(f32x16& sacc, f32x16& dpacc, float xd,
     auto elem = [&](auto ec) {
       constexpr int e = decltype(ec)::value, r = 4 * j + e;
       const bool keep = drop_keep_byte(bq[j], e, d.thr);
-      const float p = fast_exp2(sacc[r] * sl2);
+      const float p = fast_exp2(sacc[r]);
       sacc[r] = keep ? p : 0.f;
       dpacc[r] = p * fmaf(keep ? d.scale : 0.f, dpacc[r], row_bcast<r>(xd));
     };
@@ -431,7 +433,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
 #pragma unroll
   for (int i = 0; i < ND; ++i) { dkacc[i] = zero16(); dvacc[i] = zero16(); }
 
-  const float sl2 = a.scale_log2, inv_sl2 = 1.f / a.scale_log2;
   const int nqt = (s + BQ - 1) / BQ;
   const int qt0 = a.causal ? kv0 / BQ : 0;
   // Sliding window: queries past kv0 + BKV - 1 + W - 1 see none of these keys.
@@ -463,11 +464,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
     qld.template issue<true>(qsa + buf * TB, a.q + (int64_t)hq * s * D, q0, s, w, lane);
     dold.template issue<true>(dosa + buf * TB, a.dout + (int64_t)hq * D, q0, s, w, lane);
   };
-  // Stored negated (the LSE in units of the raw score) to seed the S and dP
-  // accumulators; rows past the end get -inf (P = 0) and 0.
+  // Stored negated to seed the S and dP accumulators (S = Q K^T is in the
+  // base-2 units of the LSE); rows past the end get -inf (P = 0) and 0.
   auto store_stats = [&](int buf) {
     if (tid < BQ) {
-      lse_s[buf][tid] = valid_r ? -lse_r * inv_sl2 : -INFINITY;
+      lse_s[buf][tid] = valid_r ? -lse_r : -INFINITY;
       dd_s[buf][tid] = valid_r ? -dd_r : 0.f;
     }
   };
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
                       (win && q0 + BQ - 1 >= kv0 + win);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // Seeding the accumulators with -lse (score units) and -D_i puts the row
+      // Seeding the accumulators with -lse and -D_i puts the row
       // statistics where the products land, with no extra registers.
       f32x16 sacc, dpacc;
       float xd;
@@ -540,12 +541,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
         // with z = scale (kept) or 0. Element r is query q0 + 32 qb +
         // 8 (r / 4) + 4 g + r % 4: one generator call per four queries.
         const int hg = a.drop.head0 + hk * a.group + pp * gp + step / per_head;
-        drop_dkdv(sacc, dpacc, xd, a.drop, (q0 + 32 * qb + 4 * g) >> 2, kvrow, hg, sl2,
+        drop_dkdv(sacc, dpacc, xd, a.drop, (q0 + 32 * qb + 4 * g) >> 2, kvrow, hg,
                   std::make_integer_sequence<int, 4>());
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[r] * sl2);
+          const float p = fast_exp2(sacc[r]);
           sacc[r] = p;
           dpacc[r] = p * dpacc[r];
         }
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kv = kv0 + 32 * w + acc_row(r, g);
-      float dkv = dkacc[i][r] * a.scale;
+      float dkv = dkacc[i][r] * a.dk_scale;
       const float pair = shfl_xor(dkv, 1);
       if (a.rope && kv < s) {
         const float2 cs = a.rope[(int64_t)kv * (D / 2) + (d >> 1)];
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
 }
 
 // dK, dV of the query-head-split pass: sums the nparts raw partials in
-// order, then applies 1/sqrt(D) and the inverse RoPE to dK as the unsplit
+// order, then applies the dK factor and the inverse RoPE to dK as the unsplit
 // kernel does, and stores both in bf16. One thread per (row, KV head, pair of
 // columns).
 template <int D>
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnBwdArgs<bf16> a) {
     const float2 pv = *(const float2*)(a.part + (2 * p + 1) * slab + off);
     k0 += pk.x; k1 += pk.y; v0 += pv.x; v1 += pv.y;
   }
-  k0 *= a.scale; k1 *= a.scale;
+  k0 *= a.dk_scale; k1 *= a.dk_scale;
   if (a.rope) {
     const float2 cs = a.rope[(int64_t)kv * (D / 2) + dp];
     const float r0 = k0 * cs.x + k1 * cs.y, r1 = k1 * cs.x - k0 * cs.y;
@@ -702,6 +703,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   }
   const float lse_q = qrow < s ? a.lse[(int64_t)hq * s + qrow] : INFINITY;
   const float dd_q = qrow < s ? a.dvec[(int64_t)hq * s + qrow] : 0.f;
+  // S^T accumulates onto -lse (Q carries log2(e)/sqrt(D), so the products
+  // are base-2 scores and P = exp2(acc)); dP^T onto -D_i (this lane's
+  // query), so dS = P * acc. With dropout, dS = P (z dP~ - D), z = scale
+  // (kept) or 0, and dP^T starts at 0. Rows past the end: P = 0.
+  f32x16 sseed, dseed;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sseed[r] = -lse_q;
+    dseed[r] = DROP ? 0.f : -dd_q;
+  }
 
   const int kv_end = a.causal ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
@@ -710,7 +721,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
   const int wave_tiles = a.causal ? wave_last / BKV + 1 : ntiles;
   const int t_lo = win ? max(0, q0 - win + 1) / BKV : 0;
   const int wave_t_lo = win ? max(0, q0 + 32 * w - win + 1) / BKV : 0;
-  const float sl2 = a.scale_log2;
 
   f32x16 dqacc[ND];
 #pragma unroll
@@ -743,11 +753,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
                         (win && kvb <= q0 + 32 * w + 31 - win);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        // dP^T accumulates onto -D_i (this lane's query), so dS = P * acc;
-        // with dropout, dS = P (z dP~ - D) with z = scale (kept) or 0.
-        f32x16 sacc = zero16(), dpacc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dpacc[r] = DROP ? 0.f : -dd_q;
+        f32x16 sacc = sseed, dpacc = dseed;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
@@ -766,12 +772,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * j + e;
               const float z = drop_keep_byte(wd, e, a.drop.thr) ? a.drop.scale : 0.f;
-              dpacc[r] = fast_exp2(fmaf(sacc[r], sl2, -lse_q)) * (z * dpacc[r] - dd_q);
+              dpacc[r] = fast_exp2(sacc[r]) * (z * dpacc[r] - dd_q);
             }
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(fmaf(sacc[r], sl2, -lse_q));
+          for (int r = 0; r < 16; ++r) dpacc[r] *= fast_exp2(sacc[r]);
         }
         if (MASK) {
           const int qc = a.causal ? min(qrow, s - 1) : s - 1;

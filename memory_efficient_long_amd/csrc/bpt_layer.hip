@@ -567,6 +567,14 @@ DropArgs drop_args(const Plan& p, int64_t head0, int64_t batch) {
   return d;
 }
 
+// The projection stores q multiplied by log2(e)/sqrt(D), the softmax's
+// scale and its change to base 2 (BPT Section 3.4, Eq. 3, evaluated with
+// exp2): every attention kernel then reads Q K^T directly as scores in base-2
+// units, and its log-sum-exp is base 2.
+inline float q_log2_scale(const Plan& p) {
+  return (float)(1.4426950408889634 / std::sqrt((double)p.D));
+}
+
 template <typename T>
 bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const T* v, T* o,
                     float* lse, int64_t head0, int64_t batch) {
@@ -574,7 +582,6 @@ bpt_status attn_fwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.drop = drop_args(p, head0, batch);
   a.q = q; a.k = k; a.v = v; a.o = o; a.ldo = p.H * p.D; a.lse = lse;
   a.s = (int)p.s; a.nh = (int)p.U; a.group = (int)p.G; a.causal = p.causal; a.window = p.window;
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const dim3 grid((unsigned)(p.U * ((p.s + 127) / 128))), blk(256);
   TimedLaunch tl(BPT_KERNEL_ATTN_FWD, st);
   // The sliding window is a compile-time variant (WIN), so the unwindowed
@@ -604,8 +611,10 @@ bpt_status attn_bwd(hipStream_t st, const Plan& p, const T* q, const T* k, const
   a.dq = dq; a.lddq = p.chunk_cols; a.dk = dk; a.dv = dv; a.lddkv = p.chunk_cols; a.rope = rope;
   a.s = (int)p.s; a.nh = (int)p.U; a.nkv = (int)p.nkvc; a.group = (int)p.G; a.causal = p.causal;
   a.window = p.window;
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  // q carries log2(e)/sqrt(D) (see q_log2_scale): dQ = dS K / sqrt(D) as
+  // usual, and dK = dS^T q / sqrt(D) = ln(2) dS^T Q for the stored Q.
   a.scale = (float)(1.0 / std::sqrt((double)p.D));
+  a.dk_scale = (float)0.6931471805599453;
   const dim3 gkv((unsigned)(p.nkvc * ((p.s + 127) / 128))), gq((unsigned)(p.U * ((p.s + 127) / 128)));
   const dim3 blk(256);
   if (p.D == 128 && sizeof(T) != 2)
@@ -681,7 +690,7 @@ bpt_status qkv_chunk(hipStream_t st, const Plan& p, const T* xn, const T* wqkv, 
                      int64_t c, T* q, T* k, T* v, const float2* rope, T* wc, T* bc) {
   const int c1 = (int)(p.U * p.D), c2 = (int)((p.U + p.nkvc) * p.D);
   if (p.U == p.H) {  // all heads in one chunk: one GEMM over the packed Q|K|V columns
-    EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv, rope, c1, c2};
+    EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv, rope, c1, c2, q_log2_scale(p)};
     BPT_TRY((gemm<T, true, false>(st, xn, p.h, wqkv, p.qkv_cols, p.s, p.qkv_cols, p.h, e,
                                   "qkv projection")));
     return BPT_OK;
@@ -702,7 +711,8 @@ bpt_status qkv_chunk(hipStream_t st, const Plan& p, const T* xn, const T* wqkv, 
                          cc.off[0], cc.off[1], cc.off[2]);
     BPT_TRY(check_launch("gather qkv chunk"));
   }
-  EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv ? bc : nullptr, rope, c1, c2};
+  EpiQKV3<T> e{q, k, v, p.s * p.D, (int)p.D, bqkv ? bc : nullptr, rope, c1, c2,
+               q_log2_scale(p)};
   BPT_TRY((gemm<T, true, false>(st, xn, p.h, wc, p.chunk_cols, p.s, p.chunk_cols, p.h, e,
                                 "qkv projection (chunk)")));
   return BPT_OK;

@@ -157,54 +157,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   epi.apply(m, n, v, 0.f, c, p);
 }
 
-// Q/K/V projection: + bias, optional RoPE on interleaved pairs, scattered to a
-// head-major [heads, s, D] buffer. Everything that depends on the column only
-// (bias, destination head and offset, rotation role) is resolved once per
-// lane in col(); each element then costs one row offset and a store.
-template <typename T>
-struct EpiQKV {
-  T* out; int64_t head_stride; int D; const T* bias; const float2* rope; int row0;
-  static constexpr bool kPair = true;
-  struct Col { float b, bp; T* dst; int rc, rot; };  // rot: 0 none, 1 even, 2 odd member
-  struct Pre { float2 cs; };
-  __device__ __forceinline__ Col col(int n) const {
-    const int head = n / D, dd = n - head * D;
-    Col c;
-    c.b = bias ? to_f32(bias[n]) : 0.f;
-    c.bp = bias ? to_f32(bias[n ^ 1]) : 0.f;
-    c.dst = out + (int64_t)head * head_stride + dd;
-    c.rc = dd >> 1;
-    c.rot = rope ? 1 + (dd & 1) : 0;
-    return c;
-  }
-  // Branches only on `rope` (uniform across the wave); the per-lane role
-  // is applied with selects.
-  __device__ __forceinline__ bool paired() const { return rope != nullptr; }
-  __device__ __forceinline__ Pre pre(int m, int, const Col& c) const {
-    if (!rope) return {{1.f, 0.f}};
-    return {rope[(int64_t)(row0 + m) * (D / 2) + c.rc]};
-  }
-  __device__ __forceinline__ void apply(int m, int, float v, float vp, const Col& c,
-                                        const Pre& p) const {
-    v += c.b;
-    if (rope) {
-      vp += c.bp;
-      const float r = c.rot == 2 ? (vp * p.cs.y + v * p.cs.x) : (v * p.cs.x - vp * p.cs.y);
-      v = c.rot ? r : v;
-    }
-    c.dst[(int64_t)m * D] = from_f32<T>(v);
-  }
-};
-
 // Q, K and V projections of all heads in one GEMM (columns [0, c1) -> q,
 // [c1, c2) -> k, [c2, N) -> v; c1, c2 multiples of D): + bias, RoPE on the
-// q and k columns, scattered to head-major [heads, s, D] buffers. Column-only
-// work is resolved in col(), as in EpiQKV.
+// q and k columns, scattered to head-major [heads, s, D] buffers. The q
+// columns are also multiplied by qmul (log2(e)/sqrt(D)) before rounding, so
+// the attention kernels' products Q K^T are scores in base-2 units and need
+// no per-element scaling. Everything that depends on the column only (bias,
+// destination, rotation role, factor) is resolved once per lane in col();
+// each element then costs one row offset and a store.
 template <typename T>
 struct EpiQKV3 {
   T* q; T* k; T* v; int64_t head_stride; int D; const T* bias; const float2* rope; int c1, c2;
+  float qmul;
   static constexpr bool kPair = true;
-  struct Col { float b, bp; T* dst; int rc, rot; };
+  struct Col { float b, bp, mul; T* dst; int rc, rot; };  // rot: 0 none, 1 even, 2 odd member
   struct Pre { float2 cs; };
   __device__ __forceinline__ Col col(int n) const {
     T* base = n < c1 ? q : (n < c2 ? k : this->v);
@@ -213,11 +179,14 @@ struct EpiQKV3 {
     Col c;
     c.b = bias ? to_f32(bias[n]) : 0.f;
     c.bp = bias ? to_f32(bias[n ^ 1]) : 0.f;
+    c.mul = n < c1 ? qmul : 1.f;
     c.dst = base + (int64_t)head * head_stride + dd;
     c.rc = dd >> 1;
     c.rot = rope && n < c2 ? 1 + (dd & 1) : 0;
     return c;
   }
+  // Branches only on `rope` (uniform across the wave); the per-lane role is
+  // applied with selects.
   __device__ __forceinline__ bool paired() const { return rope != nullptr; }
   // The rotation entry is loaded for every column when RoPE is on (v columns
   // ignore it): the address is valid for any column, and no per-lane branch
@@ -234,7 +203,7 @@ struct EpiQKV3 {
       const float r = c.rot == 2 ? (vp * p.cs.y + val * p.cs.x) : (val * p.cs.x - vp * p.cs.y);
       val = c.rot ? r : val;
     }
-    c.dst[(int64_t)m * D] = from_f32<T>(val);
+    c.dst[(int64_t)m * D] = from_f32<T>(val * c.mul);
   }
 };
 
