@@ -75,6 +75,74 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def gpu_sysfs_dir(dev):
+    """sysfs directory of the device (found by its PCI address), or None where
+    the device's clock table is not readable."""
+    try:
+        import torch
+        p = torch.cuda.get_device_properties(dev)
+        bus = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    except Exception:
+        return None
+    d = os.path.join("/sys/bus/pci/devices", bus)
+    return d if os.access(os.path.join(d, "pp_dpm_sclk"), os.R_OK) else None
+
+
+def parse_sclk(text: str):
+    """Current shader clock in MHz from a pp_dpm_sclk table (the starred
+    level, e.g. "1: 2400Mhz *"), or None."""
+    import re
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+            if m:
+                return float(m.group(1))
+    return None
+
+
+class ClockSampler:
+    """Reads the device's current shader clock from sysfs every `period` s on
+    a host thread while the timed steps run (default clocks and power; the
+    reading is what the driver reports, logged beside the timing)."""
+
+    def __init__(self, dev, period: float = 0.05):
+        import threading
+        self.dir = gpu_sysfs_dir(dev)
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True) if self.dir else None
+
+    def _run(self):
+        path = os.path.join(self.dir, "pp_dpm_sclk")
+        while not self._stop.is_set():
+            try:
+                with open(path) as fh:
+                    v = parse_sclk(fh.read())
+            except OSError:
+                return
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._thr:
+            self._thr.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thr:
+            self._stop.set()
+            self._thr.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = self.samples
+        return {"source": "sysfs pp_dpm_sclk", "samples": len(v), "mean_mhz": round(sum(v) / len(v), 1),
+                "min_mhz": min(v), "max_mhz": max(v)}
+
+
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel sources."""
@@ -536,15 +604,16 @@ def main() -> int:
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1, e2 in evs:
-        e0.record(stream)
-        fwd()
-        e1.record(stream)
-        bwd()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    with ClockSampler(dev) as clocks:
+        t0 = time.perf_counter()
+        for e0, e1, e2 in evs:
+            e0.record(stream)
+            fwd()
+            e1.record(stream)
+            bwd()
+            e2.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     timing = bpt.bpt_timing_read(reset=True)
     bpt.bpt_timing_enable([])
     fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
@@ -625,6 +694,7 @@ def main() -> int:
         "mfma_practical_frac": round(tflops / practical, 4) if practical else None,
         "fwd_ms": round(float(np.mean(fwd_ms)), 3),
         "bwd_ms": round(float(np.mean(bwd_ms)), 3),
+        "gpu_sclk": clocks.summary(),
         "kernel_ms_per_step": breakdown,
         "memory": {"saved_bytes_per_token": saved_bytes / tokens,
                    "saved_sbh": round(saved_bytes / (tokens * sh.hidden), 3),

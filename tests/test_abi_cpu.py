@@ -230,6 +230,18 @@ def test_bench_refuses_more_than_one_gpu():
     assert proc.stdout.strip() == ""
 
 
+def test_bench_clock_reading_parses_the_current_level():
+    """The bench logs the shader clock from the driver's level table: the
+    starred line is the current level; a table with none gives no reading."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    assert bench.parse_sclk("0: 500Mhz\n1: 1750Mhz *\n2: 2400Mhz\n") == 1750.0
+    assert bench.parse_sclk("S: 133Mhz\n0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.parse_sclk("") is None
+
+
 @pytest.mark.parametrize("q_block", [512, 1024, 2048, 4096, 8192])
 def test_ffn_scratch_is_a_group_of_query_blocks(q_block):
     """At s = 8192 the FFN scratch (the part of the backward workspace that
