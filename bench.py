@@ -380,8 +380,10 @@ def bench_stack(args, sh, L, k) -> int:
 
 
 def bench_lm_head(args) -> int:
-    """One step = LM-head forward (loss) + backward (dz, dW_head) over all rows,
-    inputs resident in HBM."""
+    """One step = LM-head loss + gradients (dz, dW_head) over all rows, inputs
+    resident in HBM: by default the fused call (each chunk's logits computed
+    once and kept in fp32 for its dlogits), with --lm-two-calls the forward
+    and backward calls (the backward recomputes the logits)."""
     import numpy as np
     import torch
     import memory_efficient_long_amd as bpt
@@ -403,14 +405,22 @@ def bench_lm_head(args) -> int:
     loss = torch.empty(sh.rows, dtype=torch.float32, device=dev)
     saved = torch.empty(bpt.bpt_lm_head_saved_size(d), dtype=torch.uint8, device=dev)
     wsf = torch.empty(bpt.bpt_lm_head_workspace_size(d, False), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(bpt.bpt_lm_head_workspace_size(d, True), dtype=torch.uint8, device=dev)
+    fused = not args.lm_two_calls
+    if fused:
+        wsf = wsb = torch.empty(bpt.bpt_lm_head_workspace_size(d, 2), dtype=torch.uint8, device=dev)
+    else:
+        wsb = torch.empty(bpt.bpt_lm_head_workspace_size(d, True), dtype=torch.uint8, device=dev)
     dz = torch.empty_like(z)
     dw = torch.empty(sh.hidden, sh.vocab, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
-        st = bpt.bpt_lm_head_forward(d, z, w, t, loss, saved, wsf, stream)
-        st = st or bpt.bpt_lm_head_backward(d, z, w, t, saved, g, dz, dw, wsb, False, stream)
+        if fused:
+            st = bpt.bpt_lm_head_forward_backward(d, z, w, t, g, loss, saved, dz, dw, wsf,
+                                                  False, stream)
+        else:
+            st = bpt.bpt_lm_head_forward(d, z, w, t, loss, saved, wsf, stream)
+            st = st or bpt.bpt_lm_head_backward(d, z, w, t, saved, g, dz, dw, wsb, False, stream)
         if st:
             raise bpt.BptError(st, "lm head")
 
@@ -433,7 +443,7 @@ def bench_lm_head(args) -> int:
     ms = float(np.mean(step_ms))
     n, h, V = sh.rows, sh.hidden, sh.vocab
     model = 6 * n * h * V          # logits, dz and dW products (2nhV each)
-    hw = 8 * n * h * V             # + the logits recomputed in the backward
+    hw = (6 if fused else 8) * n * h * V   # two calls: + the logits recomputed
     gm, gn = timing["lm_head"]
     achieved = model / (gm / args.steps * 1e-3) / 1e12 if gm > 0 else 0.0
     peak = PEAK_BF16_TFLOPS if sh.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -444,20 +454,25 @@ def bench_lm_head(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
         "data": "synthetic",
         "config": {"workload": sh.name, "rows": n, "hidden": h, "vocab": V,
-                   "chunk_rows": sh.chunk_rows},
+                   "chunk_rows": sh.chunk_rows,
+                   "path": "fused forward+backward" if fused else "forward, then backward"},
         "model_tflops": round(model / (ms * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "gemm_dma_kernel (LM head: logits with the log-sum-exp epilogue, "
-                               "recomputed logits with the dlogit epilogue, dz, dW)",
+                     "kernel": ("gemm_dma_kernel (LM head: logits with the log-sum-exp and "
+                                "fp32-logit epilogue, dz, dW)") if fused else
+                               ("gemm_dma_kernel (LM head: logits with the log-sum-exp epilogue, "
+                                "recomputed logits with the dlogit epilogue, dz, dW)"),
                      "avg_launch_ms": round(gm / max(gn, 1), 3),
                      "launches_per_step": gn / args.steps,
                      "kernel_ms_per_step": round(gm / args.steps, 3),
-                     "flops_unit": "6*h*V per row (model); 8*h*V per row run (logits recomputed)",
+                     "flops_unit": "6*h*V per row (model)" + ("" if fused else
+                                   "; 8*h*V per row run (logits recomputed)"),
                      "hardware_flops_per_step": hw},
         "rowwise_ms_per_step": round(timing["rowwise"][0] / args.steps, 3),
         "memory": {"saved_bytes_per_token": bpt.bpt_lm_head_saved_size(d) / n,
                    "workspace_bytes": max(wsf.numel(), wsb.numel()),
+                   "chunk_logits_fp32_bytes_held": 4 * cfg.chunk_rows * V if fused else 0,
                    "logits_fp32_bytes_not_held": 4 * n * V},
         "cpu_baseline": None,
     }
@@ -495,6 +510,8 @@ def main() -> int:
                     help="query heads per attention stage (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
+    ap.add_argument("--lm-two-calls", action="store_true",
+                    help="LM head: time the forward and backward calls instead of the fused call")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time GEMM and row-wise kernel classes (adds events)")
     ap.add_argument("--window", type=int, default=0, metavar="W",

@@ -260,8 +260,9 @@ bpt_status bpt_lm_head_validate(const bpt_lm_head_desc* desc);
 size_t bpt_lm_head_saved_size(const bpt_lm_head_desc* desc);
 
 /* Workspace bytes: forward (backward = 0) chunk_rows x (vocab / 32) (max, sum) pairs plus
- * chunk_rows floats; backward (1) chunk_rows x vocab dlogits in the storage dtype. Independent
- * of rows. Returns 0 for an invalid descriptor. */
+ * chunk_rows floats; backward (1) chunk_rows x vocab dlogits in the storage dtype; the fused
+ * call (2) both, plus chunk_rows x vocab fp32 logits and chunk_rows floats. Independent of
+ * rows. Returns 0 for an invalid descriptor or another value of `backward`. */
 size_t bpt_lm_head_workspace_size(const bpt_lm_head_desc* desc, int32_t backward);
 
 /* Forward. z: [rows, hidden] (16-byte aligned); w_head: [hidden, vocab] (16-byte aligned);
@@ -280,6 +281,22 @@ bpt_status bpt_lm_head_backward(const bpt_lm_head_desc* desc, const void* z, con
                                 const int32_t* targets, const void* saved, const float* dloss,
                                 void* dz, float* dw_head, int32_t accumulate, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* Forward and backward in one call, for callers that know each row's loss cotangent before
+ * the forward (training with a fixed reduction, e.g. dloss = 1 / number of counted rows).
+ * Same computation as bpt_lm_head_forward followed by bpt_lm_head_backward with that dloss
+ * ("Blockwise Parallel Transformer...", §3.4, handling of the cross-entropy loss): per chunk,
+ * the logits GEMM keeps the chunk's fp32 logits in the workspace next to the log-sum-exp
+ * partials, and the chunk's dlogits are formed from them, so the logits are computed once
+ * instead of twice; still nothing of size rows x vocab exists at once. Outputs: loss as the
+ * forward; saved (may be NULL) the forward's saved state; dz, dw_head and accumulate as the
+ * backward (either may be NULL, not both). ws: bpt_lm_head_workspace_size(desc, 2) bytes.
+ * Results equal the two calls' bit for bit. Same error behaviour as the other calls. */
+bpt_status bpt_lm_head_forward_backward(const bpt_lm_head_desc* desc, const void* z,
+                                        const void* w_head, const int32_t* targets,
+                                        const float* dloss, float* loss, void* saved, void* dz,
+                                        float* dw_head, int32_t accumulate, void* ws,
+                                        size_t ws_bytes, void* stream);
 
 /* ---- Kernel timing (instrumentation for benchmarks and profiling) ----
  * When a class is enabled, every launch of that kernel class is bracketed by

@@ -24,7 +24,8 @@ __all__ = [
     "bpt_layer_forward_noalloc", "bpt_layer_noalloc_scratch_bytes",
     "LmHeadConfig", "BptLmHeadDesc", "bpt_lm_head_validate", "bpt_lm_head_saved_size",
     "bpt_lm_head_workspace_size", "bpt_lm_head_forward", "bpt_lm_head_backward",
-    "lm_head_forward", "lm_head_backward", "check_lm_head_args",
+    "bpt_lm_head_forward_backward", "lm_head_forward", "lm_head_backward",
+    "lm_head_forward_backward", "check_lm_head_args",
     "StackConfig", "BptStackDesc", "bpt_stack_validate", "bpt_stack_saved_size",
     "bpt_stack_workspace_size", "bpt_stack_forward", "bpt_stack_backward", "stack_forward",
     "stack_backward",
@@ -149,6 +150,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.bpt_lm_head_backward.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                          ctypes.c_size_t, vp]
     lib.bpt_lm_head_backward.restype = ctypes.c_int
+    lib.bpt_lm_head_forward_backward.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                                 vp, ctypes.c_size_t, vp]
+    lib.bpt_lm_head_forward_backward.restype = ctypes.c_int
     lib.bpt_status_string.argtypes = [ctypes.c_int]
     lib.bpt_status_string.restype = ctypes.c_char_p
     lib.bpt_last_error.argtypes = []
@@ -495,13 +499,15 @@ def bpt_lm_head_saved_size(desc) -> int:
     return load_library().bpt_lm_head_saved_size(ctypes.byref(_lm_desc(desc)))
 
 
-def bpt_lm_head_workspace_size(desc, backward: bool) -> int:
+def bpt_lm_head_workspace_size(desc, backward) -> int:
+    """backward: False / 0 forward, True / 1 backward, 2 the fused call."""
     return load_library().bpt_lm_head_workspace_size(ctypes.byref(_lm_desc(desc)), int(backward))
 
 
 def check_lm_head_args(desc, z, w_head, targets, saved, workspace, backward, loss=None,
                        dloss=None, dz=None, dw_head=None) -> None:
-    """Raise ValueError unless every tensor matches the LM-head descriptor."""
+    """Raise ValueError unless every tensor matches the LM-head descriptor
+    (backward: 0 forward, 1 backward, 2 the fused call, whose saved may be None)."""
     d = _lm_desc(desc)
     if d.dtype not in _TORCH_DTYPE_NAMES:
         raise ValueError("descriptor dtype")
@@ -510,10 +516,13 @@ def check_lm_head_args(desc, z, w_head, targets, saved, workspace, backward, los
     dev = z.device
     _check_tensor(w_head, "w_head", dev, dtype=dt, shape=(d.hidden, d.vocab))
     _check_tensor(targets, "targets", dev, dtype="int32", numel=d.rows)
-    _check_tensor(saved, "saved", dev, min_bytes=bpt_lm_head_saved_size(d))
-    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_lm_head_workspace_size(d, backward))
-    if not backward:
+    mode = int(backward)
+    if saved is not None or mode != 2:
+        _check_tensor(saved, "saved", dev, min_bytes=bpt_lm_head_saved_size(d))
+    _check_tensor(workspace, "workspace", dev, min_bytes=bpt_lm_head_workspace_size(d, mode))
+    if mode != 1:
         _check_tensor(loss, "loss", dev, dtype="float32", numel=d.rows)
+    if mode == 0:
         return
     _check_tensor(dloss, "dloss", dev, dtype="float32", numel=d.rows)
     if dz is None and dw_head is None:
@@ -542,6 +551,18 @@ def bpt_lm_head_backward(desc, z, w_head, targets, saved, dloss, dz, dw_head, wo
     return load_library().bpt_lm_head_backward(
         ctypes.byref(d), _ptr(z), _ptr(w_head), _ptr(targets), _ptr(saved), _ptr(dloss), _ptr(dz),
         _ptr(dw_head), int(accumulate), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+
+
+def bpt_lm_head_forward_backward(desc, z, w_head, targets, dloss, loss, saved, dz, dw_head,
+                                 workspace, accumulate=False, stream=None) -> int:
+    """Raw fused call (device tensors, checked first); saved, dz or dw_head may be None."""
+    d = _lm_desc(desc)
+    check_lm_head_args(d, z, w_head, targets, saved, workspace, 2, loss=loss, dloss=dloss, dz=dz,
+                       dw_head=dw_head)
+    return load_library().bpt_lm_head_forward_backward(
+        ctypes.byref(d), _ptr(z), _ptr(w_head), _ptr(targets), _ptr(dloss), _ptr(loss),
+        _ptr(saved), _ptr(dz), _ptr(dw_head), int(accumulate), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_handle(stream))
 
 
@@ -576,6 +597,26 @@ def lm_head_backward(cfg: LmHeadConfig, z, w_head, targets, saved, dloss, dz=Non
     if st:
         raise BptError(st, "bpt_lm_head_backward")
     return dz, dw_head
+
+
+def lm_head_forward_backward(cfg: LmHeadConfig, z, w_head, targets, dloss, stream=None):
+    """loss, saved, dz, dw_head = lm_head_forward_backward(...): loss and gradients in one
+    call (the logits computed once per chunk); allocates every output."""
+    import torch
+    d = cfg.desc()
+    st = bpt_lm_head_validate(d)
+    if st:
+        raise BptError(st, "bpt_lm_head_validate")
+    loss = torch.empty(cfg.rows, dtype=torch.float32, device=z.device)
+    saved = _alloc_bytes(bpt_lm_head_saved_size(d), z.device)
+    dz = torch.empty_like(z)
+    dw_head = torch.empty(cfg.hidden, cfg.vocab, dtype=torch.float32, device=z.device)
+    ws = _alloc_bytes(bpt_lm_head_workspace_size(d, 2), z.device)
+    st = bpt_lm_head_forward_backward(d, z, w_head, targets, dloss, loss, saved, dz, dw_head, ws,
+                                      False, stream)
+    if st:
+        raise BptError(st, "bpt_lm_head_forward_backward")
+    return loss, saved, dz, dw_head
 
 
 # ----------------------------------------------------------------- stack of layers

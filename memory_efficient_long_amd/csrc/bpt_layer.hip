@@ -1155,23 +1155,28 @@ bpt_status make_lm_plan(const bpt_lm_head_desc* d, LmPlan& p) {
 }
 
 struct LmWs {
-  float2* part; float* tlogit; void* dl;
+  float2* part; float* tlogit; void* dl; float* logits; float* lse2;
 };
 
-LmWs carve_lm(Carver& c, const LmPlan& p, bool backward) {
+// mode 0: forward (partials, target logits); 1: backward (dlogits); 2: the
+// fused call (both, plus the chunk's fp32 logits and log-sum-exps).
+LmWs carve_lm(Carver& c, const LmPlan& p, int mode) {
   LmWs w{};
-  if (!backward) {
+  if (mode != 1) {
     w.part = c.take<float2>(p.c * p.nb);
     w.tlogit = c.take<float>(p.c);
-  } else {
-    w.dl = c.take<char>(p.c * p.V * p.esz);
+  }
+  if (mode != 0) w.dl = c.take<char>(p.c * p.V * p.esz);
+  if (mode == 2) {
+    w.logits = c.take<float>(p.c * p.V);
+    w.lse2 = c.take<float>(p.c);
   }
   return w;
 }
 
-size_t lm_ws_bytes(const LmPlan& p, bool backward) {
+size_t lm_ws_bytes(const LmPlan& p, int mode) {
   Carver c(nullptr);
-  carve_lm(c, p, backward);
+  carve_lm(c, p, mode);
   return c.off;
 }
 
@@ -1179,10 +1184,10 @@ template <typename T>
 bpt_status lm_forward_impl(const LmPlan& p, const T* z, const T* w, const int* tg, float* loss,
                            float* lse2, void* ws, hipStream_t st) {
   Carver c(ws);
-  LmWs wk = carve_lm(c, p, false);
+  LmWs wk = carve_lm(c, p, 0);
   for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
     const int64_t rows = std::min(p.c, p.n - r0);
-    EpiCEStats e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V};
+    EpiCEStats<> e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V, nullptr};
     BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, e, "lm logits",
                                   nullptr, 0, BPT_KERNEL_LM_HEAD)));
     TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
@@ -1199,7 +1204,7 @@ bpt_status lm_backward_impl(const LmPlan& p, const T* z, const T* w, const int* 
                             const float* lse2, const float* dloss, T* dz, float* dw,
                             int accumulate, void* ws, hipStream_t st) {
   Carver c(ws);
-  LmWs wk = carve_lm(c, p, true);
+  LmWs wk = carve_lm(c, p, 1);
   T* dl = (T*)wk.dl;
   if (dw && !accumulate) BPT_TRY(fill(st, dw, p.h * p.V, 0.f));
   for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
@@ -1207,6 +1212,47 @@ bpt_status lm_backward_impl(const LmPlan& p, const T* z, const T* w, const int* 
     EpiCEGrad<T> eg{dl, p.V, lse2 + r0, tg + r0, dloss + r0, (int)p.V};
     BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, eg,
                                   "lm logits (re) -> dlogits", nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    if (dz) {
+      EpiOut<T, T> ez{dz + r0 * p.h, p.h, nullptr, 1.f, 0};
+      BPT_TRY((gemm<T, true, true>(st, dl, p.V, w, p.V, rows, p.h, p.V, ez, "lm dz", nullptr, 0,
+                                   BPT_KERNEL_LM_HEAD)));
+    }
+    if (dw) {
+      EpiOut<T, float> ew{dw, p.V, nullptr, 1.f, 1};
+      BPT_TRY((gemm<T, false, false>(st, z + r0 * p.h, p.h, dl, p.V, p.h, p.V, rows, ew, "lm dW",
+                                     nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    }
+  }
+  return BPT_OK;
+}
+
+// Forward and backward in one pass over the chunks: the logits GEMM stores
+// the chunk's fp32 logits beside its statistics, and the dlogits come from
+// them (same arithmetic as the backward's recompute epilogue) instead of from
+// a second logits GEMM. lse2 (the saved state) may be NULL.
+template <typename T>
+bpt_status lm_fused_impl(const LmPlan& p, const T* z, const T* w, const int* tg,
+                         const float* dloss, float* loss, float* lse2, T* dz, float* dw,
+                         int accumulate, void* ws, hipStream_t st) {
+  Carver c(ws);
+  LmWs wk = carve_lm(c, p, 2);
+  T* dl = (T*)wk.dl;
+  if (dw && !accumulate) BPT_TRY(fill(st, dw, p.h * p.V, 0.f));
+  for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
+    const int64_t rows = std::min(p.c, p.n - r0);
+    float* l2 = lse2 ? lse2 + r0 : wk.lse2;
+    EpiCEStats<true> e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V, wk.logits};
+    BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, e,
+                                  "lm logits (stored)", nullptr, 0, BPT_KERNEL_LM_HEAD)));
+    {
+      TimedLaunch tl(BPT_KERNEL_ROWWISE, st);
+      hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                         wk.part, p.nb, wk.tlogit, tg + r0, (int)rows, (int)p.V, l2, loss + r0);
+      const int64_t n4 = rows * (p.V / 4);
+      hipLaunchKernelGGL((ce_dlogit_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                         st, wk.logits, l2, tg + r0, dloss + r0, (int)rows, (int)p.V, dl);
+      BPT_TRY(check_launch("ce combine / dlogits"));
+    }
     if (dz) {
       EpiOut<T, T> ez{dz + r0 * p.h, p.h, nullptr, 1.f, 0};
       BPT_TRY((gemm<T, true, true>(st, dl, p.V, w, p.V, rows, p.h, p.V, ez, "lm dz", nullptr, 0,
@@ -1395,8 +1441,8 @@ size_t bpt_lm_head_saved_size(const bpt_lm_head_desc* desc) {
 
 size_t bpt_lm_head_workspace_size(const bpt_lm_head_desc* desc, int32_t backward) {
   LmPlan p;
-  if (make_lm_plan(desc, p) != BPT_OK) return 0;
-  return lm_ws_bytes(p, backward != 0);
+  if (make_lm_plan(desc, p) != BPT_OK || backward < 0 || backward > 2) return 0;
+  return lm_ws_bytes(p, backward);
 }
 
 bpt_status bpt_lm_head_forward(const bpt_lm_head_desc* desc, const void* z, const void* w_head,
@@ -1410,7 +1456,7 @@ bpt_status bpt_lm_head_forward(const bpt_lm_head_desc* desc, const void* z, cons
   if (!aligned16(z) || !aligned16(w_head) || ((uintptr_t)targets & 3) || ((uintptr_t)loss & 3) ||
       ((uintptr_t)saved & 3) || ((uintptr_t)ws & 255))
     return fail(BPT_EINVAL, "z, w_head 16-byte, targets/loss/saved 4-byte, ws 256-byte aligned");
-  if (ws_bytes < lm_ws_bytes(p, false)) return fail(BPT_EWORKSPACE, "workspace too small");
+  if (ws_bytes < lm_ws_bytes(p, 0)) return fail(BPT_EWORKSPACE, "workspace too small");
   hipStream_t st = (hipStream_t)stream;
   if (p.dtype == BPT_BF16)
     return lm_forward_impl<bf16>(p, (const bf16*)z, (const bf16*)w_head, targets, loss,
@@ -1434,7 +1480,7 @@ bpt_status bpt_lm_head_backward(const bpt_lm_head_desc* desc, const void* z, con
       ((uintptr_t)saved & 3) || ((uintptr_t)dloss & 3) || ((uintptr_t)dw_head & 3) ||
       ((uintptr_t)ws & 255))
     return fail(BPT_EINVAL, "z, w_head, dz 16-byte, targets/saved/dloss/dw_head 4-byte, ws 256-byte aligned");
-  if (ws_bytes < lm_ws_bytes(p, true)) return fail(BPT_EWORKSPACE, "workspace too small");
+  if (ws_bytes < lm_ws_bytes(p, 1)) return fail(BPT_EWORKSPACE, "workspace too small");
   hipStream_t st = (hipStream_t)stream;
   if (p.dtype == BPT_BF16)
     return lm_backward_impl<bf16>(p, (const bf16*)z, (const bf16*)w_head, targets,
@@ -1443,6 +1489,32 @@ bpt_status bpt_lm_head_backward(const bpt_lm_head_desc* desc, const void* z, con
   return lm_backward_impl<float>(p, (const float*)z, (const float*)w_head, targets,
                                  (const float*)saved, dloss, (float*)dz, dw_head, accumulate, ws,
                                  st);
+}
+
+bpt_status bpt_lm_head_forward_backward(const bpt_lm_head_desc* desc, const void* z,
+                                        const void* w_head, const int32_t* targets,
+                                        const float* dloss, float* loss, void* saved, void* dz,
+                                        float* dw_head, int32_t accumulate, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  LmPlan p;
+  BPT_TRY(make_lm_plan(desc, p));
+  if (!z || !w_head || !targets || !dloss || !loss || !ws)
+    return fail(BPT_EINVAL, "z, w_head, targets, dloss, loss and ws must be non-NULL");
+  if (!dz && !dw_head) return fail(BPT_EINVAL, "dz and dw_head are both NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(BPT_EINVAL, "accumulate must be 0 or 1");
+  if (!aligned16(z) || !aligned16(w_head) || (dz && !aligned16(dz)) || ((uintptr_t)targets & 3) ||
+      ((uintptr_t)dloss & 3) || ((uintptr_t)loss & 3) || ((uintptr_t)saved & 3) ||
+      ((uintptr_t)dw_head & 3) || ((uintptr_t)ws & 255))
+    return fail(BPT_EINVAL,
+                "z, w_head, dz 16-byte, targets/dloss/loss/saved/dw_head 4-byte, ws 256-byte aligned");
+  if (ws_bytes < lm_ws_bytes(p, 2)) return fail(BPT_EWORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  if (p.dtype == BPT_BF16)
+    return lm_fused_impl<bf16>(p, (const bf16*)z, (const bf16*)w_head, targets, dloss, loss,
+                               (float*)saved, (bf16*)dz, dw_head, accumulate, ws, st);
+  return lm_fused_impl<float>(p, (const float*)z, (const float*)w_head, targets, dloss, loss,
+                              (float*)saved, (float*)dz, dw_head, accumulate, ws, st);
 }
 
 const char* bpt_status_string(bpt_status s) {

@@ -11,6 +11,11 @@
 //   backward: the same GEMM again, with dlogit = g (2^(x - lse2) - [n == t])
 //             written for the chunk only, then dz = dlogits W^T and
 //             dW += z^T dlogits (ordinary GEMMs).
+//   fused   : (forward and backward in one call, the cotangents g known
+//             before the forward) the forward's GEMM also stores the chunk's
+//             fp32 logits; after the combine, ce_dlogit_kernel forms the
+//             chunk's dlogits from them with the backward epilogue's
+//             arithmetic, so the logits GEMM runs once per chunk.
 //
 // Statistics are kept in base 2 (x = logit * log2 e); lse2 is the base-2
 // log-sum-exp, loss = lse2 ln 2 - logit[t]. A target outside [0, V) marks an
@@ -59,13 +64,15 @@ __device__ __forceinline__ void rs_step(float (&m)[16], float (&l)[16], int lr) 
 }
 
 // Forward epilogue: log-sum-exp partials per (row, 32-column block) and the
-// target logit of each row.
+// target logit of each row; STORE: the fp32 logits too (the fused call).
+template <bool STORE = false>
 struct EpiCEStats {
   float2* part;        // [M, nb]: (max, sum) in base-2 units
   int64_t nb;          // 32-column blocks per row
   float* tlogit;       // [M]: logit of the row's target (raw, natural units)
   const int* targets;  // [M]
   int V;               // vocabulary size (columns >= V are not logits)
+  float* logits;       // STORE: [M, V] raw logits (row stride V)
   static constexpr bool kPair = false;
   struct Col {};
   struct Pre {};
@@ -75,9 +82,9 @@ struct EpiCEStats {
 // of rows m0 + acc_row(r, g), r < 16. A reduce-scatter over the 32 lanes of
 // the half-wave leaves lanes lr and lr ^ 1 with row (lr >> 1) merged over all
 // 32 columns; the even one stores the pair.
-template <bool EVEN>
-__device__ __forceinline__ void epilogue_block(const EpiCEStats& e, const f32x16& acc, int m0,
-                                               int col, int g, int M, int) {
+template <bool EVEN, bool STORE>
+__device__ __forceinline__ void epilogue_block(const EpiCEStats<STORE>& e, const f32x16& acc,
+                                               int m0, int col, int g, int M, int) {
   const int lr = col & 31;  // block columns start at multiples of 32
   const bool cvalid = col < e.V;
   int tg[16];
@@ -93,6 +100,8 @@ __device__ __forceinline__ void epilogue_block(const EpiCEStats& e, const f32x16
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + acc_row(r, g);
     if (cvalid && row < M && tg[r] == col) e.tlogit[row] = acc[r];
+    if constexpr (STORE)
+      if (cvalid && row < M) e.logits[(int64_t)row * e.V + col] = acc[r];
   }
   rs_step<16, 8>(m, l, lr);
   rs_step<8, 4>(m, l, lr);
@@ -105,8 +114,17 @@ __device__ __forceinline__ void epilogue_block(const EpiCEStats& e, const f32x16
     e.part[(int64_t)row * e.nb + (col >> 5)] = make_float2(m[0], l[0]);
 }
 
-// Backward epilogue: dlogit = g (softmax - onehot(t)) from the recomputed
-// logit and the forward's base-2 log-sum-exp; 0 on ignored rows.
+// dlogit = g (softmax - onehot(t)) of logit v in column n from the base-2
+// log-sum-exp; 0 on ignored rows. Shared by the backward epilogue and the
+// fused call's kernel, so both produce the same bits.
+__device__ __forceinline__ float ce_dlogit(float v, int n, float lse2, float g, int t, int V) {
+  const bool valid = t >= 0 && t < V;
+  const float q = fast_exp2(fmaf(v, kLog2e, -lse2)) - (n == t ? 1.f : 0.f);
+  return valid ? q * g : 0.f;
+}
+
+// Backward epilogue: dlogit from the recomputed logit and the forward's
+// base-2 log-sum-exp.
 template <typename T>
 struct EpiCEGrad {
   T* dl; int64_t ldo; const float* lse2; const int* targets; const float* dloss; int V;
@@ -119,11 +137,31 @@ struct EpiCEGrad {
   }
   __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
                                         const Pre& p) const {
-    const bool valid = p.t >= 0 && p.t < V;
-    const float q = fast_exp2(fmaf(v, kLog2e, -p.lse2)) - (n == p.t ? 1.f : 0.f);
-    dl[(int64_t)m * ldo + n] = from_f32<T>(valid ? q * p.g : 0.f);
+    dl[(int64_t)m * ldo + n] = from_f32<T>(ce_dlogit(v, n, p.lse2, p.g, p.t, V));
   }
 };
+
+// Fused call: dlogits [rows, V] of a chunk from its stored fp32 logits. One
+// thread per four consecutive columns of a row (V is a multiple of 64).
+template <typename T>
+__global__ __launch_bounds__(256) void ce_dlogit_kernel(const float* __restrict__ logits,
+                                                        const float* __restrict__ lse2,
+                                                        const int* __restrict__ targets,
+                                                        const float* __restrict__ dloss, int rows,
+                                                        int V, T* __restrict__ dl) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int v4 = V / 4;
+  if (q >= (int64_t)rows * v4) return;
+  const int row = (int)(q / v4), n0 = (int)(q - (int64_t)row * v4) * 4;
+  const float l2 = lse2[row], g = dloss[row];
+  const int t = targets[row];
+  const float4 x = *(const float4*)(logits + (int64_t)row * V + n0);
+  T* o = dl + (int64_t)row * V + n0;
+  o[0] = from_f32<T>(ce_dlogit(x.x, n0, l2, g, t, V));
+  o[1] = from_f32<T>(ce_dlogit(x.y, n0 + 1, l2, g, t, V));
+  o[2] = from_f32<T>(ce_dlogit(x.z, n0 + 2, l2, g, t, V));
+  o[3] = from_f32<T>(ce_dlogit(x.w, n0 + 3, l2, g, t, V));
+}
 
 // Per row: merge the nb partial pairs into the base-2 log-sum-exp (saved for
 // the backward) and the loss. One wave per row, four rows per workgroup.

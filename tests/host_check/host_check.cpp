@@ -167,14 +167,34 @@ void check_lm(int64_t rows, int64_t h, int64_t V, int64_t chunk, int32_t dtype, 
   const bpt_status v = bpt_lm_head_validate(&d);
   const size_t saved = bpt_lm_head_saved_size(&d);
   const size_t wf = bpt_lm_head_workspace_size(&d, 0), wb = bpt_lm_head_workspace_size(&d, 1);
+  const size_t wfb = bpt_lm_head_workspace_size(&d, 2);
+  expect(bpt_lm_head_workspace_size(&d, 3) == 0 && bpt_lm_head_workspace_size(&d, -1) == 0,
+         "LM head workspace of an unknown mode", "non-zero");
   if (v == BPT_OK) {
     ++valid;
-    expect(saved > 0 && wf > 0 && wb > 0, "sizes of a valid LM head", "zero size");
+    expect(saved > 0 && wf > 0 && wb > 0 && wfb > wf + wb, "sizes of a valid LM head",
+           "zero size");
     bpt_status r = bpt_lm_head_forward(&d, dummy, dummy, nullptr, (float*)(void*)dummy, dummy, dummy, wf,
                                        nullptr);
     expect(r == BPT_EINVAL, "LM head forward with NULL targets", bpt_status_string(r));
+    float* fd = (float*)(void*)dummy;
+    r = bpt_lm_head_forward_backward(&d, dummy, dummy, (const int32_t*)(void*)dummy, fd, fd,
+                                     nullptr, nullptr, nullptr, 0, dummy, wfb, nullptr);
+    expect(r == BPT_EINVAL, "fused LM head with neither dz nor dw_head", bpt_status_string(r));
+    r = bpt_lm_head_forward_backward(&d, dummy, dummy, (const int32_t*)(void*)dummy, fd, fd,
+                                     nullptr, dummy, nullptr, 0, dummy, wfb - 1, nullptr);
+    expect(r == BPT_EWORKSPACE, "fused LM head with a short workspace", bpt_status_string(r));
+    r = bpt_lm_head_forward_backward(&d, dummy, dummy, (const int32_t*)(void*)dummy, fd, fd,
+                                     nullptr, dummy, nullptr, 2, dummy, wfb, nullptr);
+    expect(r == BPT_EINVAL, "fused LM head with accumulate = 2", bpt_status_string(r));
   } else {
-    expect(saved == 0 && wf == 0 && wb == 0, "sizes of an invalid LM head", bpt_last_error());
+    expect(saved == 0 && wf == 0 && wb == 0 && wfb == 0, "sizes of an invalid LM head",
+           bpt_last_error());
+    const bpt_status r = bpt_lm_head_forward_backward(&d, dummy, dummy, nullptr, nullptr, nullptr,
+                                                      nullptr, dummy, nullptr, 0, dummy,
+                                                      sizeof dummy, nullptr);
+    expect(r != BPT_OK && r != BPT_EHIP, "fused LM head with an invalid descriptor",
+           bpt_status_string(r));
   }
 }
 

@@ -230,6 +230,67 @@ def test_bench_refuses_more_than_one_gpu():
     assert proc.stdout.strip() == ""
 
 
+def test_lm_head_workspace_modes():
+    """The fused LM-head call's workspace holds the forward's and the
+    backward's plus one chunk's fp32 logits and log-sum-exps (each region
+    rounded up to 256 bytes); other modes are refused with 0."""
+    def up(n):
+        return (n + 255) // 256 * 256
+    for rows, h, v, c in [(1000, 128, 512, 256), (37, 64, 64, 64), (131072, 2048, 50304, 8192)]:
+        cfg = bpt.LmHeadConfig(rows=rows, hidden=h, vocab=v, chunk_rows=c)
+        cc = min(c, (rows + 63) // 64 * 64)
+        f, b, fb = (bpt.bpt_lm_head_workspace_size(cfg, m) for m in (0, 1, 2))
+        assert f == up(cc * (v // 32) * 8) + up(cc * 4)
+        assert b == up(cc * v * 2)
+        assert fb == f + b + up(cc * v * 4) + up(cc * 4)
+        assert bpt.bpt_lm_head_workspace_size(cfg, 3) == 0
+        assert bpt.bpt_lm_head_workspace_size(cfg, -1) == 0
+
+
+def test_lm_head_fused_binding_checks(monkeypatch):
+    """The fused call's binding refuses mismatched tensors before any launch;
+    saved may be None, dz and dw_head not both."""
+    torch = pytest.importorskip("torch")
+    lib = bpt.load_library()
+    calls = []
+    monkeypatch.setattr(lib, "bpt_lm_head_forward_backward", lambda *a: calls.append(1) or 0)
+    monkeypatch.setattr(bpt, "DEVICE_TYPE", "cpu")
+    cfg = bpt.LmHeadConfig(rows=100, hidden=64, vocab=128, chunk_rows=64)
+    d = cfg.desc()
+    z = torch.zeros(100, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 128, dtype=torch.bfloat16)
+    t = torch.zeros(100, dtype=torch.int32)
+    g = torch.zeros(100, dtype=torch.float32)
+    loss = torch.zeros(100, dtype=torch.float32)
+    dz = torch.zeros_like(z)
+    dw = torch.zeros(64, 128, dtype=torch.float32)
+    ws = torch.zeros(bpt.bpt_lm_head_workspace_size(d, 2), dtype=torch.uint8)
+    saved = torch.zeros(bpt.bpt_lm_head_saved_size(d), dtype=torch.uint8)
+    st = _Stream()
+    assert bpt.bpt_lm_head_forward_backward(d, z, w, t, g, loss, saved, dz, dw, ws, stream=st) == 0
+    assert bpt.bpt_lm_head_forward_backward(d, z, w, t, g, loss, None, None, dw, ws, stream=st) == 0
+    assert len(calls) == 2
+    bad = {
+        "ws-short": dict(ws=ws[:-1]),
+        "ws-of-backward": dict(ws=torch.zeros(bpt.bpt_lm_head_workspace_size(d, 1),
+                                              dtype=torch.uint8)),
+        "loss-short": dict(loss=loss[:-1]),
+        "dloss-missing": dict(g=None),
+        "dloss-bf16": dict(g=g.bfloat16()),
+        "saved-short": dict(saved=saved[:-4]),
+        "no-grads": dict(dz=None, dw=None),
+        "dw-bf16": dict(dw=dw.bfloat16()),
+        "targets-int64": dict(t=t.long()),
+    }
+    for name, change in bad.items():
+        a = dict(z=z, w=w, t=t, g=g, loss=loss, saved=saved, dz=dz, dw=dw, ws=ws)
+        a.update(change)
+        with pytest.raises(ValueError):
+            bpt.bpt_lm_head_forward_backward(d, a["z"], a["w"], a["t"], a["g"], a["loss"],
+                                             a["saved"], a["dz"], a["dw"], a["ws"], stream=st)
+        assert len(calls) == 2, name
+
+
 def test_bench_clock_reading_parses_the_current_level():
     """The bench logs the shader clock from the driver's level table: the
     starred line is the current level; a table with none gives no reading."""

@@ -6,6 +6,9 @@ against the float64 oracle (oracle/lm_head_oracle.py).
 * Peaked logits (W_head scaled 16x): the row log-sum-exp is dominated by a few
   columns far from the block maxima of the others.
 * dW accumulation across calls; bitwise reproducibility.
+* The fused forward + backward call: bit for bit the two calls' results
+  (with and without the saved state, dz or dW alone, accumulating), guard
+  regions around its outputs and workspace.
 * The benchmarked shape (131072 rows, hidden 2048, vocabulary 50304): loss at
   sampled rows, and the backward from a cotangent on those rows only (dz must
   be exactly zero elsewhere; dW is the sum over the sampled rows).
@@ -62,6 +65,29 @@ def _run_gpu(inp, accumulate_into=None):
     dz, dw = bpt.lm_head_backward(cfg, z, w, t, saved, g)
     torch.cuda.synchronize()
     return {"loss": loss, "saved": saved, "dz": dz, "dw": dw}
+
+
+def _run_fused(inp, saved=True, dz=True, dw=True, dw_init=None):
+    import memory_efficient_long_amd as bpt
+    sh = inp.sh
+    cfg = bpt.LmHeadConfig(sh.rows, sh.hidden, sh.vocab, sh.chunk_rows, sh.dtype)
+    d = cfg.desc()
+    z, w = _dev(inp.z), _dev(inp.w)
+    t = torch.from_numpy(inp.t).cuda()
+    g = torch.from_numpy(inp.g).cuda()
+    loss = torch.empty(sh.rows, dtype=torch.float32, device="cuda")
+    sv = torch.empty(bpt.bpt_lm_head_saved_size(d), dtype=torch.uint8, device="cuda") if saved else None
+    dzt = torch.empty_like(z) if dz else None
+    dwt = None
+    if dw:
+        dwt = (dw_init.clone() if dw_init is not None
+               else torch.empty(sh.hidden, sh.vocab, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(bpt.bpt_lm_head_workspace_size(d, 2), dtype=torch.uint8, device="cuda")
+    st = bpt.bpt_lm_head_forward_backward(d, z, w, t, g, loss, sv, dzt, dwt, ws,
+                                          accumulate=dw_init is not None)
+    assert st == 0, bpt.bpt_last_error()
+    torch.cuda.synchronize()
+    return {"loss": loss, "saved": sv, "dz": dzt, "dw": dwt}
 
 
 def _errs(gpu, ref, rows=None):
@@ -142,6 +168,48 @@ def test_lm_head_accumulate_and_reproducible():
     assert err < 1e-6
 
 
+@pytest.mark.parametrize("name", ["lmhead-small-f32", "lmhead-small-bf16"])
+@pytest.mark.parametrize("w_scale", [1.0, 16.0])
+def test_lm_head_fused_equals_two_calls(name, w_scale):
+    """The fused call forms each chunk's dlogits from the stored fp32 logits
+    with the backward epilogue's arithmetic: its loss, saved state, dz and dW
+    equal the forward + backward calls' bit for bit (and so meet the oracle
+    bars those calls are held to, checked here again)."""
+    from oracle import lm_head_oracle as lmo
+    sh = wl.LM_HEADS[name]
+    _say(f"[lm-head fused] {name} W x{w_scale}")
+    inp = LmInputs(sh, w_scale)
+    two = _run_gpu(inp)
+    fused = _run_fused(inp)
+    for k in ("loss", "saved", "dz", "dw"):
+        assert torch.equal(two[k], fused[k]), k
+    ref = lmo.lm_head_ce(inp.z.f64(), inp.w.f64(), inp.t, inp.g.astype(np.float64))
+    errs = _errs(fused, ref)
+    _say(f"  errs {errs}")
+    bad = over_bar(errs, sh.dtype)
+    assert not bad, bad
+
+
+def test_lm_head_fused_options():
+    """Without the saved state, with dz or dW alone, and accumulating into dW:
+    the same bits as the full fused call (twice dW when accumulating onto it)."""
+    sh = wl.LM_HEADS["lmhead-small-bf16"]
+    _say(f"[lm-head fused options] {sh.name}")
+    inp = LmInputs(sh)
+    full = _run_fused(inp)
+    a = _run_fused(inp, saved=False)
+    assert torch.equal(a["loss"], full["loss"]) and torch.equal(a["dz"], full["dz"])
+    assert torch.equal(a["dw"], full["dw"])
+    b = _run_fused(inp, dw=False)
+    assert torch.equal(b["dz"], full["dz"]) and torch.equal(b["saved"], full["saved"])
+    c = _run_fused(inp, dz=False)
+    assert torch.equal(c["dw"], full["dw"])
+    e = _run_fused(inp, dw_init=full["dw"])
+    assert torch.equal(e["dz"], full["dz"])
+    err = (e["dw"].double() - 2 * full["dw"].double()).norm() / (2 * full["dw"].double()).norm()
+    assert err < 1e-6
+
+
 def test_lm_head_no_writes_outside_outputs():
     """loss, saved, dz, dW and both workspaces, each sized exactly, between
     guard regions that must come back untouched."""
@@ -177,6 +245,19 @@ def test_lm_head_no_writes_outside_outputs():
     ref = _run_gpu(inp)
     assert torch.equal(loss, ref["loss"]) and torch.equal(dz, ref["dz"])
     assert torch.equal(dw, ref["dw"])
+    # the fused call: the same outputs and its own workspace, each guarded
+    n0 = len(bufs)
+    loss2 = guarded(sh.rows, torch.float32)
+    saved2 = guarded(bpt.bpt_lm_head_saved_size(d), torch.uint8)
+    ws_fb = guarded(bpt.bpt_lm_head_workspace_size(d, 2), torch.uint8)
+    dz2 = guarded(z.numel(), z.dtype, z.shape)
+    dw2 = guarded(sh.hidden * sh.vocab, torch.float32, (sh.hidden, sh.vocab))
+    assert bpt.bpt_lm_head_forward_backward(d, z, w, t, g, loss2, saved2, dz2, dw2, ws_fb) == 0
+    torch.cuda.synchronize()
+    for buf in bufs[n0:]:
+        assert torch.all(buf[:guard] == 7) and torch.all(buf[-guard:] == 7)
+    assert torch.equal(loss2, ref["loss"]) and torch.equal(saved2, ref["saved"])
+    assert torch.equal(dz2, ref["dz"]) and torch.equal(dw2, ref["dw"])
 
 
 @pytest.mark.slow
@@ -203,3 +284,8 @@ def test_lm_head_full_size_sampled_rows():
     other = np.ones(sh.rows, bool)
     other[rows] = False
     assert np.all(to_host64(gpu["dz"])[other] == 0.0)
+    # the fused call at full size: the same bits as the two calls
+    _say("  fused call at full size")
+    fused = _run_fused(inp)
+    for k in ("loss", "saved", "dz", "dw"):
+        assert torch.equal(gpu[k], fused[k]), k
