@@ -389,6 +389,8 @@ def bench_lm_head(args) -> int:
     import memory_efficient_long_amd as bpt
     import workloads as wl
     sh = wl.LM_HEADS[args.workload]
+    if args.lm_chunk_rows:
+        sh = sh.replace(chunk_rows=args.lm_chunk_rows)
     dev = torch.device("cuda:0")
 
     def to_dev(t):
@@ -510,6 +512,8 @@ def main() -> int:
                     help="query heads per attention stage (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=8192)
+    ap.add_argument("--lm-chunk-rows", type=int, default=0,
+                    help="LM head: rows per chunk (default: the workload's)")
     ap.add_argument("--lm-two-calls", action="store_true",
                     help="LM head: time the forward and backward calls instead of the fused call")
     ap.add_argument("--breakdown", action="store_true",
