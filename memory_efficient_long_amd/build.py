@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
 ]
 
 
+# roctx ranges (only emitted when BPT_ROCTX=1; see the host code).
+LINK_FLAGS = ["-lrocprofiler-sdk-roctx"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,7 +44,7 @@ def build(verbose: bool = False, out: str = LIB_PATH, csrc: str = CSRC, defines=
     src = os.path.join(csrc, "bpt_layer.hip")
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(REPO, "include"),
-           src, "-o", tmp]
+           src, "-o", tmp, *LINK_FLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

@@ -17,9 +17,12 @@
 // per head chunk recompute Q, K, V and run the attention backward, the QKV
 // weight gradient and dxn; finally Norm1's backward plus the residual.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <atomic>
 #include <mutex>
@@ -51,6 +54,53 @@ bpt_status fail(bpt_status st, const std::string& msg) {
     bpt_status _st = (expr);                           \
     if (_st != BPT_OK) return _st;                     \
   } while (0)
+
+// ---- Optional instrumentation, switched by environment variables read once:
+// BPT_ROCTX=1 brackets every phase (layer forward / backward, head chunk, FFN
+// group, stack layer, LM-head chunk) with a roctx range, which `rocprofv3
+// --marker-trace` records next to the kernels; BPT_LOG=1 prints each call's
+// plan (shape, chunks, groups, buffer sizes) to stderr. Both are off by
+// default and cost one branch per phase then.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+bool markers_on() {
+  static const bool on = env_on("BPT_ROCTX");
+  return on;
+}
+bool log_on() {
+  static const bool on = env_on("BPT_LOG");
+  return on;
+}
+
+struct Range {
+  bool on;
+  explicit Range(const char* fmt, ...) : on(markers_on()) {
+    if (!on) return;
+    char buf[128];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    roctxRangePush(buf);
+  }
+  ~Range() {
+    if (on) roctxRangePop();
+  }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
+void log_line(const char* fmt, ...) {
+  if (!log_on()) return;
+  va_list ap;
+  va_start(ap, fmt);
+  std::fputs("[bpt] ", stderr);
+  std::vfprintf(stderr, fmt, ap);
+  std::fputc('\n', stderr);
+  va_end(ap);
+}
 
 bpt_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
@@ -185,6 +235,15 @@ bpt_status make_plan(const bpt_layer_desc* d, Plan& p) {
 // Largest query-head split of the dK/dV pass that the workspace provides for:
 // a power of two dividing G, at most kDkvMaxParts, for bf16 with head_dim 64
 // or 128 and fewer than 8 KV heads per chunk (more give enough workgroups).
+void log_plan(const char* what, const Plan& p, size_t ws_bytes) {
+  log_line("%s: b=%lld s=%lld h=%lld heads=%lld/%lld d=%lld ffn=%lld %s, head chunk %lld "
+           "(%lld chunks), FFN groups of %lld rows, causal=%d window=%d dropout_thr=%d, "
+           "workspace %zu bytes", what, (long long)p.b, (long long)p.s, (long long)p.h,
+           (long long)p.H, (long long)p.Hkv, (long long)p.D, (long long)p.f,
+           p.dtype == BPT_BF16 ? "bf16" : "fp32", (long long)p.U, (long long)(p.H / p.U),
+           (long long)(p.gq * p.cq), p.causal, p.window, p.drop_thr, ws_bytes);
+}
+
 int dkv_parts_max(const Plan& p) {
   if (p.dtype != BPT_BF16 || (p.D != 64 && p.D != 128) || p.nkvc >= 8) return 1;
   int m = 1;
@@ -736,6 +795,7 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
   float* LSE = (float*)((char*)saved + align_up((size_t)(p.b * p.s * HD) * p.esz, 256));
   BPT_TRY(rope_table(st, p, w.rope));
   const int act = p.ffn == BPT_RELU ? ACT_RELU : ACT_GELU;
+  Range r_all("bpt layer forward (s=%lld)", (long long)p.s);
 
   for (int64_t bi = 0; bi < p.b; ++bi) {
     const T* xb = x + bi * p.s * p.h;
@@ -744,6 +804,7 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
     float* Lb = LSE + bi * p.H * p.s;
     BPT_TRY((norm_fwd<T, T, T>(st, p, xb, p.h, g1, sh1, w.xn, p.h, p.s)));
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
+      Range r_ch("forward: projection and attention, head chunk %lld", (long long)ch);
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
       BPT_TRY(attn_fwd<T>(st, p, w.q, w.k, w.v, Ob + ch * p.U * p.D, Lb + ch * p.U * p.s,
                           ch * p.U, bi));
@@ -753,6 +814,8 @@ bpt_status forward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt, 
     const int64_t grp = p.gq * p.cq;
     for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
       const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
+      Range r_g("forward: O projection, Norm2, FFN, rows %lld-%lld", (long long)g0,
+                (long long)(g0 + rows));
       const float* h1g = w.h1;
       {
         EpiResid<T, T, float> eo{w.h1, p.h, xb + g0 * p.h, p.h, bo};
@@ -814,6 +877,7 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     BPT_TRY(fill(st, dg2, p.h, 0.f)); BPT_TRY(fill(st, dsh2, p.h, 0.f));
   }
   BPT_TRY(rope_table(st, p, w.rope));
+  Range r_all("bpt layer backward (s=%lld)", (long long)p.s);
 
   for (int64_t bi = 0; bi < p.b; ++bi) {
     const T* xb = x + bi * p.s * p.h;
@@ -830,6 +894,8 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     const int64_t grp = p.gq * p.cq;
     for (int64_t g0 = 0; g0 < p.s; g0 += grp) {
       const int64_t rows = std::min(grp, p.s - g0);  // a multiple of c_q
+      Range r_g("backward: FFN and Norm2 (recomputed), rows %lld-%lld", (long long)g0,
+                (long long)(g0 + rows));
       const T* dyg = dyb + g0 * p.h;
       const float* h1g = w.h1;
       {
@@ -918,6 +984,8 @@ bpt_status backward_impl(const Plan& p, const T* x, const bpt_layer_weights* wt,
     BPT_TRY(check_launch("attn_dvec"));
     }
     for (int64_t ch = 0; ch < p.H / p.U; ++ch) {
+      Range r_ch("backward: projection (recomputed), attention and QKV, head chunk %lld",
+                 (long long)ch);
       const int64_t hq0 = ch * p.U, hk0 = hq0 / p.G;
       BPT_TRY(qkv_chunk<T>(st, p, w.xn, wqkv, bqkv, ch, w.q, w.k, w.v, w.rope, w.wc, w.bc));
       T* dK = w.dqkv + p.U * p.D;
@@ -1075,6 +1143,7 @@ bpt_status stack_forward_impl(const StackPlan& sp, const T* x, const bpt_layer_w
     else if ((l + 1) % sp.k == 0) out = (T*)(saved + (size_t)((l + 1) / sp.k - 1) * sp.act);
     else out = (T*)pp[l & 1];
     void* lsaved = sp.k ? (void*)tsaved : (void*)(saved + (size_t)sp.nck * sp.act + l * sp.sv);
+    Range r_l("stack forward: layer %lld", (long long)l);
     BPT_TRY(forward_impl<T>(sp.lp, cur, &w[l], out, lsaved, lws, st));
     cur = out;
   }
@@ -1103,6 +1172,7 @@ bpt_status stack_backward_impl(const StackPlan& sp, const T* x, const bpt_layer_
       for (int64_t i = 0; i < cnt; ++i) {
         T* out = i < cnt - 1 ? (T*)(seg_in + (size_t)i * sp.act) : (T*)scratch;
         void* lsv = seg_sv + (size_t)i * sp.sv;
+        Range r_l("stack backward: layer %lld recomputed", (long long)(l0 + i));
         BPT_TRY(forward_impl<T>(sp.lp, in[i], &w[l0 + i], out, lsv, lws, st));
         in[i + 1] = out;
         sv[i] = lsv;
@@ -1117,6 +1187,7 @@ bpt_status stack_backward_impl(const StackPlan& sp, const T* x, const bpt_layer_
     for (int64_t i = cnt - 1; i >= 0; --i) {
       const int64_t l = l0 + i;
       T* g_out = l == 0 ? dx : (T*)(g_cur == (const T*)gb[0] ? gb[1] : gb[0]);
+      Range r_l("stack backward: layer %lld", (long long)l);
       BPT_TRY(backward_impl<T>(sp.lp, in[i], &w[l], sv[i], g_cur, g_out, &gr[l], lws, st));
       g_cur = g_out;
     }
@@ -1187,6 +1258,7 @@ bpt_status lm_forward_impl(const LmPlan& p, const T* z, const T* w, const int* t
   LmWs wk = carve_lm(c, p, 0);
   for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
     const int64_t rows = std::min(p.c, p.n - r0);
+    Range r_c("lm head forward: rows %lld-%lld", (long long)r0, (long long)(r0 + rows));
     EpiCEStats<> e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V, nullptr};
     BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, e, "lm logits",
                                   nullptr, 0, BPT_KERNEL_LM_HEAD)));
@@ -1209,6 +1281,7 @@ bpt_status lm_backward_impl(const LmPlan& p, const T* z, const T* w, const int* 
   if (dw && !accumulate) BPT_TRY(fill(st, dw, p.h * p.V, 0.f));
   for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
     const int64_t rows = std::min(p.c, p.n - r0);
+    Range r_c("lm head backward: rows %lld-%lld", (long long)r0, (long long)(r0 + rows));
     EpiCEGrad<T> eg{dl, p.V, lse2 + r0, tg + r0, dloss + r0, (int)p.V};
     BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, eg,
                                   "lm logits (re) -> dlogits", nullptr, 0, BPT_KERNEL_LM_HEAD)));
@@ -1240,6 +1313,7 @@ bpt_status lm_fused_impl(const LmPlan& p, const T* z, const T* w, const int* tg,
   if (dw && !accumulate) BPT_TRY(fill(st, dw, p.h * p.V, 0.f));
   for (int64_t r0 = 0; r0 < p.n; r0 += p.c) {
     const int64_t rows = std::min(p.c, p.n - r0);
+    Range r_c("lm head forward+backward: rows %lld-%lld", (long long)r0, (long long)(r0 + rows));
     float* l2 = lse2 ? lse2 + r0 : wk.lse2;
     EpiCEStats<true> e{wk.part, p.nb, wk.tlogit, tg + r0, (int)p.V, wk.logits};
     BPT_TRY((gemm<T, true, false>(st, z + r0 * p.h, p.h, w, p.V, rows, p.V, p.h, e,
@@ -1299,6 +1373,7 @@ bpt_status bpt_layer_forward(const bpt_layer_desc* desc, const void* x, const bp
   if (!aligned16(x) || !aligned16(y) || !aligned16(saved) || ((uintptr_t)ws & 255))
     return fail(BPT_EINVAL, "x, y, saved must be 16-byte and ws 256-byte aligned");
   if (ws_bytes < fwd_ws_bytes(p)) return fail(BPT_EWORKSPACE, "workspace too small");
+  log_plan("bpt_layer_forward", p, fwd_ws_bytes(p));
   hipStream_t st = (hipStream_t)stream;
   if (p.dtype == BPT_BF16)
     return forward_impl<bf16>(p, (const bf16*)x, w, (bf16*)y, saved, ws, st);
@@ -1323,6 +1398,7 @@ bpt_status bpt_layer_forward_noalloc(const bpt_layer_desc* desc, const void* x,
                                     " (use bpt_layer_forward with a workspace)");
   void* ws = nullptr;
   BPT_TRY(scratch_address(&ws));
+  log_plan("bpt_layer_forward_noalloc", p, need);
   hipStream_t st = (hipStream_t)stream;
   if (p.dtype == BPT_BF16)
     return forward_impl<bf16>(p, (const bf16*)x, w, (bf16*)y, saved, ws, st);
@@ -1352,6 +1428,7 @@ bpt_status bpt_layer_backward(const bpt_layer_desc* desc, const void* x, const b
   for (const float* g : gp)
     if (g && ((uintptr_t)g & 3)) return fail(BPT_EINVAL, "gradient buffer misaligned");
   if (ws_bytes < bwd_ws_bytes(p)) return fail(BPT_EWORKSPACE, "workspace too small");
+  log_plan("bpt_layer_backward", p, bwd_ws_bytes(p));
   hipStream_t st = (hipStream_t)stream;
   if (p.dtype == BPT_BF16)
     return backward_impl<bf16>(p, (const bf16*)x, w, saved, (const bf16*)dy, (bf16*)dx, grads, ws,

@@ -10,11 +10,14 @@ must be refused before any launch. No GPU is made visible to the run.
 import os
 import shutil
 import subprocess
+import sys
 
 import pytest
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+sys.path.insert(0, REPO)
+from memory_efficient_long_amd.build import LINK_FLAGS  # noqa: E402
 
 # Each sanitizer flag is preceded by -Xarch_host: host code only.
 SANITIZE = ["-Xarch_host", "-fsanitize=address",
@@ -30,7 +33,8 @@ def test_host_code_under_asan_ubsan(tmp_path):
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result",
            "-I", os.path.join(REPO, "include"),
            os.path.join(REPO, "tests", "host_check", "host_check.cpp"),
-           os.path.join(REPO, "memory_efficient_long_amd", "csrc", "bpt_layer.hip"), "-o", exe]
+           os.path.join(REPO, "memory_efficient_long_amd", "csrc", "bpt_layer.hip"), "-o", exe,
+           *LINK_FLAGS]
     build = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
     assert build.returncode == 0, build.stderr[-4000:]
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ASAN_OPTIONS="detect_leaks=0",
