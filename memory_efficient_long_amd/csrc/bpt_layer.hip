@@ -555,8 +555,9 @@ bpt_status norm_bwd(hipStream_t st, const Plan& p, const float* dz, int64_t lddz
   if (!finish) return BPT_OK;
   const int P = *nparts;
   const dim3 g2((unsigned)((p.h + 63) / 64));
-  if (dg) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pg, P, (int)p.h, dg, 1);
-  if (db) hipLaunchKernelGGL(colsum_final_kernel, g2, blk, 0, st, pb, P, (int)p.h, db, 1);
+  const dim3 bf(64 * kColsumFinalLanes);
+  if (dg) hipLaunchKernelGGL(colsum_final_kernel, g2, bf, 0, st, pg, P, (int)p.h, dg, 1);
+  if (db) hipLaunchKernelGGL(colsum_final_kernel, g2, bf, 0, st, pb, P, (int)p.h, db, 1);
   return check_launch("norm_bwd reduce");
 }
 
@@ -582,8 +583,8 @@ bpt_status colsum(hipStream_t st, const Tin* X, int64_t ldx, int64_t rows, int64
     P = *nparts;
   }
   if (finish && P > 0)
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, st,
-                       part, P, (int)N, out, 1);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 63) / 64)),
+                       dim3(64 * kColsumFinalLanes), 0, st, part, P, (int)N, out, 1);
   return check_launch("colsum");
 }
 

@@ -310,26 +310,37 @@ __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __re
   }
 }
 
-// Stage 2: out[col] (+)= sum_p part[p, col]; block = 64 columns x 4 partial
-// lanes, each lane summing every 4th partial row, then an LDS reduction.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int P,
-                                                           int N, float* out, int accumulate) {
-  __shared__ float red[4][64];
+// Stage 2: out[col] (+)= sum_p part[p, col]; block = 64 columns x 16
+// partial lanes (1024 threads), each lane summing every 16th partial row with
+// up to 16 of its loads in flight at a time, then an LDS reduction. (With 4
+// lanes per column and its loads waited for one by one, the reduction of the
+// norm backward's 2048 partial rows took ~40-60 us per call on 32 blocks.)
+constexpr int kColsumFinalLanes = 16;
+__global__ __launch_bounds__(64 * kColsumFinalLanes) void colsum_final_kernel(
+    const float* __restrict__ part, int P, int N, float* out, int accumulate) {
+  constexpr int L = kColsumFinalLanes, U = 16;
+  __shared__ float red[L][64];
   const int cl = threadIdx.x & 63, rl = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + cl;
-  float a0 = 0.f, a1 = 0.f;
+  float a = 0.f;
   if (col < N) {
-    int p = rl;
-    for (; p + 4 < P; p += 8) {
-      a0 += part[(int64_t)p * N + col];
-      a1 += part[(int64_t)(p + 4) * N + col];
+    for (int p0 = rl; p0 < P; p0 += L * U) {
+      float v[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int p = p0 + L * i;
+        v[i] = p < P ? part[(int64_t)p * N + col] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) a += v[i];
     }
-    if (p < P) a0 += part[(int64_t)p * N + col];
   }
-  red[rl][cl] = a0 + a1;
+  red[rl][cl] = a;
   __syncthreads();
   if (rl == 0 && col < N) {
-    const float acc = red[0][cl] + red[1][cl] + red[2][cl] + red[3][cl];
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) acc += red[j][cl];
     out[col] = accumulate ? out[col] + acc : acc;
   }
 }
