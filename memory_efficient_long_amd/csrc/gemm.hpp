@@ -71,29 +71,80 @@ __device__ __forceinline__ float lane_xor1(float v) {
 // Each epilogue is applied to one 32 x 32 accumulator block of a lane (one
 // column, 16 rows) in three steps: col(n) loads what depends on the column
 // only (a bias), pre(m, n, col) gathers each element's other inputs
-// (residual, previous value, ...) for all 16 rows, then apply(...) computes
-// and stores. Gathering first, unconditionally from clamped indices, matters
+// (residual, previous value, ...) for all 16 rows, then the values are
+// computed and stored. Gathering first, unconditionally from clamped indices, matters
 // on this GPU: vector-memory loads and stores share one in-order counter, so
 // a load issued after stores -- or inside its own branch -- cannot be waited
 // for without also waiting for everything before it. v is the fp32
 // accumulator value; vp, when kPair, the value of column n ^ 1 in the same
 // row (used by the RoPE rotation).
+//
+// The computing and storing are split: an epilogue has kOuts outputs of
+// element type Out; value(o, ...) is what output o holds at (m, n) (before
+// rounding to Out) and dst(o, m, n) its address, with 16 / sizeof(Out)
+// consecutive columns (from a multiple of that count) contiguous in memory
+// whenever vec_ok(16 / sizeof(Out)) holds; has(o) says whether output o is
+// written at all. epi_apply stores one element; the direct-load GEMM also
+// stores whole 16-byte row pieces (see epilogue_staged), with the same values.
+
+__device__ __forceinline__ bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// a, b or c (b when b1, c when also b2) by address arithmetic: a select among
+// neighbouring pointer fields of an epilogue becomes a load at a computed
+// offset, which keeps the whole epilogue object in scratch memory.
+template <typename P>
+__device__ __forceinline__ P* pick3(P* a, P* b, P* c, bool b1, bool b2) {
+  const uintptr_t ua = (uintptr_t)a, ub = (uintptr_t)b, uc = (uintptr_t)c;
+  return (P*)(ua + (b1 ? ub - ua : 0) + (b2 ? uc - ub : 0));
+}
+
+// Epilogues whose outputs the direct-load GEMM stages through LDS: those with
+// the value/dst interface that ask for it (kStaged) and have 2-byte outputs
+// (a half-wave's fp32 row segment, 32 columns, is already a whole 128-byte
+// line; staging it measured slower).
+template <class E, class = void>
+struct staged_outputs : std::false_type {};
+template <class E>
+struct staged_outputs<E, std::void_t<decltype(E::kOuts)>>
+    : std::bool_constant<E::kStaged && sizeof(typename E::Out) == 2> {};
+
+// Store through a global-memory pointer (an output address computed by
+// integer arithmetic would otherwise be stored to as a generic one).
+template <typename V>
+__device__ __forceinline__ void st_global(V* p, V v) {
+  *(__attribute__((address_space(1))) V*)p = v;
+}
+
+template <class Epi>
+__device__ __forceinline__ void epi_apply(const Epi& e, int m, int n, float v, float vp,
+                                          const typename Epi::Col& c,
+                                          const typename Epi::Pre& p) {
+#pragma unroll
+  for (int o = 0; o < Epi::kOuts; ++o)
+    if (e.has(o)) st_global(e.dst(o, m, n), from_f32<typename Epi::Out>(e.value(o, m, n, v, vp, c, p)));
+}
 
 // out = alpha * v (+ bias[n]) (+ out if accumulate)
 template <typename T, typename OutT>
 struct EpiOut {
   OutT* out; int64_t ldo; const T* bias; float alpha; int accumulate;
   static constexpr bool kPair = false;
+  using Out = OutT;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col { float b; };
   struct Pre { float o; };
   __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
   __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {accumulate ? to_f32(out[(int64_t)m * ldo + n]) : 0.f};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
-                                        const Pre& p) const {
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(fmaf(alpha, v, c.b + p.o));
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const { return al16(out) && ldo % vec == 0; }
+  __device__ __forceinline__ float value(int, int, int, float v, float, const Col& c,
+                                         const Pre& p) const {
+    return fmaf(alpha, v, c.b + p.o);
   }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return out + (int64_t)m * ldo + n; }
 };
 
 // out_k[m, n - start_k] (+)= v for the three column segments [0, c1),
@@ -104,18 +155,28 @@ template <typename T>
 struct EpiOut3 {
   float* out0; float* out1; float* out2; int64_t ldo; int c1, c2; int accumulate;
   static constexpr bool kPair = false;
+  using Out = float;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col { float* dst; };
   struct Pre { float o; };
-  __device__ __forceinline__ Col col(int n) const {
-    return {n < c1 ? out0 + n : (n < c2 ? out1 + (n - c1) : out2 + (n - c2))};
+  __device__ __forceinline__ float* seg(int n) const {
+    return pick3(out0, out1, out2, n >= c1, n >= c2) + (n < c1 ? n : (n < c2 ? n - c1 : n - c2));
   }
+  __device__ __forceinline__ Col col(int n) const { return {seg(n)}; }
   __device__ __forceinline__ Pre pre(int m, int, const Col& c) const {
     return {accumulate ? c.dst[(int64_t)m * ldo] : 0.f};
   }
-  __device__ __forceinline__ void apply(int m, int, float v, float, const Col& c,
-                                        const Pre& p) const {
-    c.dst[(int64_t)m * ldo] = v + p.o;
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(out0) && al16(out1) && al16(out2) && ldo % vec == 0 && c1 % vec == 0 &&
+           c2 % vec == 0;
   }
+  __device__ __forceinline__ float value(int, int, int, float v, float, const Col&,
+                                         const Pre& p) const {
+    return v + p.o;
+  }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return seg(n) + (int64_t)m * ldo; }
 };
 
 // Split-K partial product: copy k of the split grid writes its raw fp32 sum
@@ -124,14 +185,22 @@ struct EpiOut3 {
 struct EpiPart {
   float* out; int64_t ldo; int64_t split_stride;
   static constexpr bool kPair = false;
+  using Out = float;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col {};
   struct Pre {};
   __device__ __forceinline__ Col col(int) const { return {}; }
   __device__ __forceinline__ Pre pre(int, int, const Col&) const { return {}; }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
-                                        const Pre&) const {
-    out[(int64_t)m * ldo + n] = v;
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(out) && ldo % vec == 0 && split_stride % vec == 0;
   }
+  __device__ __forceinline__ float value(int, int, int, float v, float, const Col&,
+                                         const Pre&) const {
+    return v;
+  }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return out + (int64_t)m * ldo + n; }
 };
 template <class Epi>
 __device__ __forceinline__ Epi epi_at_split(const Epi& e, int) { return e; }
@@ -154,7 +223,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int k = 0; k < nsplit; ++k) v += part[k * mn + i];
   const typename Epi::Col c = epi.col(n);
   const typename Epi::Pre p = epi.pre(m, n, c);
-  epi.apply(m, n, v, 0.f, c, p);
+  epi_apply(epi, m, n, v, 0.f, c, p);
 }
 
 // Q, K and V projections of all heads in one GEMM (columns [0, c1) -> q,
@@ -164,23 +233,24 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // the attention kernels' products Q K^T are scores in base-2 units and need
 // no per-element scaling. Everything that depends on the column only (bias,
 // destination, rotation role, factor) is resolved once per lane in col();
-// each element then costs one row offset and a store.
+// each element then costs its arithmetic and a store.
 template <typename T>
 struct EpiQKV3 {
   T* q; T* k; T* v; int64_t head_stride; int D; const T* bias; const float2* rope; int c1, c2;
   float qmul;
   static constexpr bool kPair = true;
-  struct Col { float b, bp, mul; T* dst; int rc, rot; };  // rot: 0 none, 1 even, 2 odd member
+  using Out = T;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
+  struct Col { float b, bp, mul; int rc, rot; };  // rot: 0 none, 1 even, 2 odd member
   struct Pre { float2 cs; };
   __device__ __forceinline__ Col col(int n) const {
-    T* base = n < c1 ? q : (n < c2 ? k : this->v);
     const int nn = n < c1 ? n : (n < c2 ? n - c1 : n - c2);
-    const int head = nn / D, dd = nn - head * D;
+    const int dd = nn % D;
     Col c;
     c.b = bias ? to_f32(bias[n]) : 0.f;
     c.bp = bias ? to_f32(bias[n ^ 1]) : 0.f;
     c.mul = n < c1 ? qmul : 1.f;
-    c.dst = base + (int64_t)head * head_stride + dd;
     c.rc = dd >> 1;
     c.rot = rope && n < c2 ? 1 + (dd & 1) : 0;
     return c;
@@ -195,15 +265,25 @@ struct EpiQKV3 {
     if (!rope) return {{1.f, 0.f}};
     return {rope[(int64_t)m * (D / 2) + c.rc]};
   }
-  __device__ __forceinline__ void apply(int m, int, float val, float vp, const Col& c,
-                                        const Pre& p) const {
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(q) && al16(k) && al16(this->v) && head_stride % vec == 0 && D % vec == 0;
+  }
+  __device__ __forceinline__ float value(int, int, int, float val, float vp, const Col& c,
+                                         const Pre& p) const {
     val += c.b;
     if (rope) {
       vp += c.bp;
       const float r = c.rot == 2 ? (vp * p.cs.y + val * p.cs.x) : (val * p.cs.x - vp * p.cs.y);
       val = c.rot ? r : val;
     }
-    c.dst[(int64_t)m * D] = from_f32<T>(val * c.mul);
+    return val * c.mul;
+  }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const {
+    const int nn = n < c1 ? n : (n < c2 ? n - c1 : n - c2);
+    const int head = nn / D, dd = nn - head * D;
+    return pick3(q, k, this->v, n >= c1, n >= c2) + (int64_t)head * head_stride +
+           (int64_t)m * D + dd;
   }
 };
 
@@ -212,16 +292,22 @@ template <typename T, typename ResT, typename OutT>
 struct EpiResid {
   OutT* out; int64_t ldo; const ResT* res; int64_t ldr; const T* bias;
   static constexpr bool kPair = false;
+  using Out = OutT;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col { float b; };
   struct Pre { float r; };
   __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
   __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {to_f32(res[(int64_t)m * ldr + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
-                                        const Pre& p) const {
-    out[(int64_t)m * ldo + n] = from_f32<OutT>(v + c.b + p.r);
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const { return al16(out) && ldo % vec == 0; }
+  __device__ __forceinline__ float value(int, int, int, float v, float, const Col& c,
+                                         const Pre& p) const {
+    return v + c.b + p.r;
   }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return out + (int64_t)m * ldo + n; }
 };
 
 // a = v + bias[n]; optionally keep a; u = act(a)
@@ -229,16 +315,24 @@ template <typename T>
 struct EpiAct {
   T* u; T* a_keep; int64_t ldo; const T* bias; int act;
   static constexpr bool kPair = false;
+  using Out = T;
+  static constexpr int kOuts = 2;  // u, then a (kept when a_keep is given)
+  static constexpr bool kStaged = true;
   struct Col { float b; };
   struct Pre {};
   __device__ __forceinline__ Col col(int n) const { return {bias ? to_f32(bias[n]) : 0.f}; }
   __device__ __forceinline__ Pre pre(int, int, const Col&) const { return {}; }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col& c,
-                                        const Pre&) const {
+  __device__ __forceinline__ bool has(int o) const { return o == 0 || a_keep != nullptr; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(u) && (!a_keep || al16(a_keep)) && ldo % vec == 0;
+  }
+  __device__ __forceinline__ float value(int o, int, int, float v, float, const Col& c,
+                                         const Pre&) const {
     v += c.b;
-    const int64_t i = (int64_t)m * ldo + n;
-    if (a_keep) a_keep[i] = from_f32<T>(v);
-    u[i] = from_f32<T>(act == ACT_RELU ? act_relu(v) : act_gelu(v));
+    return o == 1 ? v : (act == ACT_RELU ? act_relu(v) : act_gelu(v));
+  }
+  __device__ __forceinline__ Out* dst(int o, int m, int n) const {
+    return (o == 0 ? u : a_keep) + (int64_t)m * ldo + n;
   }
 };
 
@@ -247,17 +341,25 @@ template <typename T>
 struct EpiSwiUp {
   T* u; T* up_keep; const T* gate; int64_t ldo;
   static constexpr bool kPair = false;
+  using Out = T;
+  static constexpr int kOuts = 2;  // u, then the up projection (kept when up_keep is given)
+  static constexpr bool kStaged = true;
   struct Col {};
   struct Pre { float g; };
   __device__ __forceinline__ Col col(int) const { return {}; }
   __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {to_f32(gate[(int64_t)m * ldo + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
-                                        const Pre& p) const {
-    const int64_t i = (int64_t)m * ldo + n;
-    if (up_keep) up_keep[i] = from_f32<T>(v);
-    u[i] = from_f32<T>(p.g * sigmoidf_(p.g) * v);
+  __device__ __forceinline__ bool has(int o) const { return o == 0 || up_keep != nullptr; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(u) && (!up_keep || al16(up_keep)) && ldo % vec == 0;
+  }
+  __device__ __forceinline__ float value(int o, int, int, float v, float, const Col&,
+                                         const Pre& p) const {
+    return o == 1 ? v : p.g * sigmoidf_(p.g) * v;
+  }
+  __device__ __forceinline__ Out* dst(int o, int m, int n) const {
+    return (o == 0 ? u : up_keep) + (int64_t)m * ldo + n;
   }
 };
 
@@ -266,17 +368,23 @@ template <typename T>
 struct EpiActGrad {
   T* da; const T* a; int64_t ldo; int act;
   static constexpr bool kPair = false;
+  using Out = T;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col {};
   struct Pre { float x; };
   __device__ __forceinline__ Col col(int) const { return {}; }
   __device__ __forceinline__ Pre pre(int m, int n, const Col&) const {
     return {to_f32(a[(int64_t)m * ldo + n])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
-                                        const Pre& p) const {
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const { return al16(da) && ldo % vec == 0; }
+  __device__ __forceinline__ float value(int, int, int, float v, float, const Col&,
+                                         const Pre& p) const {
     const float gr = act == ACT_RELU ? (p.x > 0.f ? 1.f : 0.f) : act_gelu_grad(p.x);
-    da[(int64_t)m * ldo + n] = from_f32<T>(v * gr);
+    return v * gr;
   }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return da + (int64_t)m * ldo + n; }
 };
 
 // SwiGLU backward from du = v: d gate = du * up * s(g) (1 + g (1 - s(g))),
@@ -285,6 +393,10 @@ template <typename T>
 struct EpiSwiGrad {
   T* dgate; T* dup; const T* gate; const T* up; int64_t ldo;
   static constexpr bool kPair = false;
+  using Out = T;
+  static constexpr int kOuts = 2;  // d gate, d up
+  // Staging measured slower here (two gathered inputs, two outputs).
+  static constexpr bool kStaged = false;
   struct Col {};
   struct Pre { float g, u; };
   __device__ __forceinline__ Col col(int) const { return {}; }
@@ -292,12 +404,17 @@ struct EpiSwiGrad {
     const int64_t i = (int64_t)m * ldo + n;
     return {to_f32(gate[i]), to_f32(up[i])};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
-                                        const Pre& p) const {
-    const int64_t i = (int64_t)m * ldo + n;
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const {
+    return al16(dgate) && al16(dup) && ldo % vec == 0;
+  }
+  __device__ __forceinline__ float value(int o, int, int, float v, float, const Col&,
+                                         const Pre& p) const {
     const float sg = sigmoidf_(p.g);
-    dgate[i] = from_f32<T>(v * p.u * sg * (1.f + p.g * (1.f - sg)));
-    dup[i] = from_f32<T>(v * p.g * sg);
+    return o == 0 ? v * p.u * sg * (1.f + p.g * (1.f - sg)) : v * p.g * sg;
+  }
+  __device__ __forceinline__ Out* dst(int o, int m, int n) const {
+    return (o == 0 ? dgate : dup) + (int64_t)m * ldo + n;
   }
 };
 
@@ -321,7 +438,7 @@ __device__ __forceinline__ void epilogue_block(const Epi& epi, const f32x16& acc
     const float v = acc[r];
     float vp = 0.f;
     if constexpr (Epi::kPair) vp = epi.paired() ? lane_xor1(v) : 0.f;
-    if (EVEN || (row < M && col < N)) epi.apply(row, col, v, vp, cv, pre[r]);
+    if (EVEN || (row < M && col < N)) epi_apply(epi, row, col, v, vp, cv, pre[r]);
   }
 }
 

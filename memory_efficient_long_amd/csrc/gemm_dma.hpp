@@ -159,6 +159,75 @@ struct Operand<false, R, BK> {
 
 }  // namespace gdma
 
+// Staged epilogue, for epilogues with the value/dst interface (gemm.hpp):
+// each wave writes its results, rounded to the output type, into its own LDS
+// region (the stage buffers, free once every wave is past the main loop) and
+// reads them back as 16-byte row pieces, so that one store instruction moves
+// 16 bytes per lane instead of one 2- or 4-byte element per lane. The values
+// are those of epi_apply, bit for bit.
+//
+// The region holds the wave's WM rows at 128 bytes each: one pass covers
+// 32 JP columns of every output (JP = 2 for a single 2-byte output, else 1).
+// The 16-byte pieces of row r are XOR-permuted by (r & 4): the two lane
+// halves of an accumulator write (rows r and r + 4, 64 bytes each) then fall
+// on different banks.
+template <int WM, int FM, int FN, class Epi>
+__device__ __forceinline__ void epilogue_staged(const Epi& e, const f32x16 (&acc)[FM][FN],
+                                                char* region, int mw, int nw, int lane, int M,
+                                                int N) {
+  using U = typename Epi::Out;
+  constexpr int ES = (int)sizeof(U), KO = Epi::kOuts;
+  constexpr int JP = (KO * ES == 2 && FN % 2 == 0) ? 2 : 1;
+  constexpr int OB = 32 * JP * ES;  // bytes of one output in a staged row
+  static_assert(KO * OB <= 128, "a staged row holds 128 bytes");
+  constexpr int PPO = OB / 16, VEC = 16 / ES, ITER = WM * PPO / 64;
+  static_assert(WM * PPO % 64 == 0, "whole pieces per lane");
+  const int lr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int jp = 0; jp < FN; jp += JP) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < JP; ++jj) {
+        const int col = nw + 32 * (jp + jj) + lr, cq = min(col, N - 1);
+        const typename Epi::Col cv = e.col(cq);
+        typename Epi::Pre pre[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          pre[r] = e.pre(min(mw + 32 * i + acc_row(r, g), M - 1), cq, cv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * i + acc_row(r, g);
+          const float x = acc[i][jp + jj][r];
+          float xp = 0.f;
+          if constexpr (Epi::kPair) xp = e.paired() ? lane_xor1(x) : 0.f;
+#pragma unroll
+          for (int o = 0; o < KO; ++o) {
+            const int b = o * OB + (32 * jj + lr) * ES;
+            *(U*)(region + rl * 128 + (((b >> 4) ^ (rl & 4)) << 4) + (b & 15)) =
+                from_f32<U>(e.value(o, mw + rl, col, x, xp, cv, pre[r]));
+          }
+        }
+      }
+    // LDS operations of a wave complete in order; the wait keeps the reads
+    // below from being scheduled above the writes.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int o = 0; o < KO; ++o) {
+      if (!e.has(o)) continue;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int idx = it * 64 + lane, rl = idx / PPO, pc = idx % PPO;
+        const u32x4 val = ld<u32x4>(region + rl * 128 + (((o * PPO + pc) ^ (rl & 4)) << 4));
+        const int m = mw + rl, n = nw + 32 * jp + pc * VEC;
+        if (m < M && n < N) st_global((u32x4*)e.dst(o, m, n), val);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // NW waves (64 NW threads) arranged (BM / WM) x (BN / WN); LDS (STAGES stages
 // of the A and B tiles) is dynamic: STAGES * (BM + BN) * BK * 2 bytes.
 template <bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int STAGES, int WM, int WN, int NW,
@@ -258,6 +327,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_dma_kernel(const bf16* __restric
 
   const int lr = lane & 31;
   const Epi e = epi_at_split(epi, split);
+  if constexpr (staged_outputs<Epi>::value) {
+    constexpr int VEC = 16 / (int)sizeof(typename Epi::Out);
+    static_assert(NW * WM * 128 <= STAGES * SBYTES, "staging regions fit the stage buffers");
+    if (N % VEC == 0 && e.vec_ok(VEC)) {
+      __syncthreads();  // every wave is past its last fragment read
+      epilogue_staged<WM>(e, acc, smem + w * WM * 128, m0 + wm0, n0 + wn0, lane, M, N);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -129,16 +129,22 @@ template <typename T>
 struct EpiCEGrad {
   T* dl; int64_t ldo; const float* lse2; const int* targets; const float* dloss; int V;
   static constexpr bool kPair = false;
+  using Out = T;
+  static constexpr int kOuts = 1;
+  static constexpr bool kStaged = true;
   struct Col {};
   struct Pre { float lse2, g; int t; };
   __device__ __forceinline__ Col col(int) const { return {}; }
   __device__ __forceinline__ Pre pre(int m, int, const Col&) const {
     return {lse2[m], dloss[m], targets[m]};
   }
-  __device__ __forceinline__ void apply(int m, int n, float v, float, const Col&,
-                                        const Pre& p) const {
-    dl[(int64_t)m * ldo + n] = from_f32<T>(ce_dlogit(v, n, p.lse2, p.g, p.t, V));
+  __device__ __forceinline__ bool has(int) const { return true; }
+  __device__ __forceinline__ bool vec_ok(int vec) const { return al16(dl) && ldo % vec == 0; }
+  __device__ __forceinline__ float value(int, int, int n, float v, float, const Col&,
+                                         const Pre& p) const {
+    return ce_dlogit(v, n, p.lse2, p.g, p.t, V);
   }
+  __device__ __forceinline__ Out* dst(int, int m, int n) const { return dl + (int64_t)m * ldo + n; }
 };
 
 // Fused call: dlogits [rows, V] of a chunk from its stored fp32 logits. One
