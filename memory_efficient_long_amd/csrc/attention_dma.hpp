@@ -224,6 +224,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
           sacc[sb] = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc[sb]);
+      // Order hint (sched_group_barrier; 0x100 = LDS reads, 0x008 = MFMA):
+      // each K fragment is read two MFMAs before its use instead of right
+      // before it (the same hint on the P V products measured slower).
+      {
+        constexpr int PF = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * NC - PF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+      }
       if (MASK) {  // wave-uniform; keys past min(query, s - 1), or W or more before it, get -inf
         const int qc = a.causal ? min(qrow, s - 1) : s - 1;
         const int lim = qc - kvb;
@@ -525,9 +538,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_dma_kernel(AttnBwdArgs<b
       // Order hint (sched_group_barrier; 0x100 = LDS reads, 0x008 = MFMA): the
       // two statistics reads and the first PF fragment reads, then each MFMA
       // followed by the next fragment read, so a read is issued PF MFMAs before
-      // its use instead of right before it.
+      // its use instead of right before it (3 measured best of 2-4; 2 in the
+      // split window variant, where a third read in flight spills).
       {
-        constexpr int PF = 2;
+        constexpr int PF = SPLIT && WIN ? 2 : 3;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 + PF, 0);
 #pragma unroll
         for (int m = 0; m < 2 * NC - PF; ++m) {
@@ -759,6 +773,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
           sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
           dpacc = mma(TL::frag_at(vsa + buf * TB, rf, sb, c), df[c], dpacc);
         }
+        // Order hints as in the dK/dV pass: K and V fragments read two MFMAs
+        // ahead here, the K^T pairs of the dQ products below likewise (not
+        // with dropout, whose extra registers they would spill).
+        if constexpr (!DROP) {
+          constexpr int PF = 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+          for (int m = 0; m < 2 * NC - PF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+        }
         if constexpr (DROP) {
           const int hg = a.drop.head0 + hq;
           // key group (kvb + 32 sb + 8 j + 4 g) / 4, shared by the quad
@@ -796,6 +823,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
           const bf16x8 dsf = pack_frag<bf16>(td);
 #pragma unroll
           for (int i = 0; i < ND; ++i) dqacc[i] = mma(TL::tr_at(ksa + buf * TB, trb, cc, i), dsf, dqacc[i]);
+        }
+        if constexpr (!DROP) {
+          constexpr int PF = 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+          for (int m = 0; m < 2 * ND - PF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
         }
       }
     }
