@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
           sacc[sb] = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc[sb]);
       // Order hint (sched_group_barrier; 0x100 = LDS reads, 0x008 = MFMA):
       // each K fragment is read two MFMAs before its use instead of right
-      // before it (the same hint on the P V products measured slower).
+      // before it.
       {
         constexpr int PF = 2;
         __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
@@ -326,6 +326,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_dma_kernel(AttnFwdArgs<bf16> 
 #pragma unroll
         for (int i = 0; i < ND; ++i)
           oacc[i] = mma(TL::template tr_at<false>(vsa + buf * TB, trb, cc, i), pf[cc], oacc[i]);
+      // The V^T pair of each product one MFMA ahead (two measured slower).
+      {
+        constexpr int PF = 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int m = 0; m < 4 * ND - PF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+      }
     }
     wait_dma();
     __syncthreads();
@@ -773,11 +784,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_dma_kernel(AttnBwdArgs<bf1
           sacc = mma(TL::frag_at(ksa + buf * TB, rf, sb, c), qf[c], sacc);
           dpacc = mma(TL::frag_at(vsa + buf * TB, rf, sb, c), df[c], dpacc);
         }
-        // Order hints as in the dK/dV pass: K and V fragments read two MFMAs
-        // ahead here, the K^T pairs of the dQ products below likewise (not
+        // Order hints as in the dK/dV pass: K and V fragments read three
+        // MFMAs ahead here, the K^T pairs of the dQ products below two (not
         // with dropout, whose extra registers they would spill).
         if constexpr (!DROP) {
-          constexpr int PF = 2;
+          constexpr int PF = 3;
           __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
           for (int m = 0; m < 2 * NC - PF; ++m) {
