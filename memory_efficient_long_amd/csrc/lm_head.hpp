@@ -96,12 +96,32 @@ __device__ __forceinline__ void epilogue_block(const EpiCEStats<STORE>& e, const
     m[r] = cvalid ? acc[r] * kLog2e : -INFINITY;
     l[r] = cvalid ? 1.f : 0.f;
   }
+  // The target logits: a row's target falls in one 32-column block of the
+  // ~V / 32, so almost every wave skips the per-element stores on one test.
+  bool hit = false;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = m0 + acc_row(r, g);
-    if (cvalid && row < M && tg[r] == col) e.tlogit[row] = acc[r];
-    if constexpr (STORE)
-      if (cvalid && row < M) e.logits[(int64_t)row * e.V + col] = acc[r];
+  for (int r = 0; r < 16; ++r) hit |= tg[r] == col;
+  if (__any(hit) && cvalid) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + acc_row(r, g);
+      if (row < M && tg[r] == col) e.tlogit[row] = acc[r];
+    }
+  }
+  if constexpr (STORE) {
+    // cvalid and m0 + 32 <= M are uniform over the wave: a whole block of
+    // logits is stored without per-element guards.
+    if (cvalid && m0 + 32 <= M) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        e.logits[(int64_t)(m0 + acc_row(r, g)) * e.V + col] = acc[r];
+    } else if (cvalid) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + acc_row(r, g);
+        if (row < M) e.logits[(int64_t)row * e.V + col] = acc[r];
+      }
+    }
   }
   rs_step<16, 8>(m, l, lr);
   rs_step<8, 4>(m, l, lr);
