@@ -176,6 +176,15 @@ SMALL: Dict[str, LayerShape] = {
         name="f32-d64-gqa-rope-noncausal", seq_len=240, hidden=256, n_heads=4, n_kv_heads=2,
         head_dim=64, ffn_dim=512, norm="rmsnorm", ffn="gelu", causal=False,
         rope_base=10000.0, q_block=120, kv_block=80, head_chunk=2),
+    # Hidden, FFN and Q/K/V widths that are not multiples of the GEMM column
+    # tile (320, 1344 and 960 / 448 columns): a partial column tile in every
+    # projection, with the GeLU and the SwiGLU epilogues.
+    "bf16-ragged-cols": WORKLOADS["gpt1b-s8k"].replace(
+        name="bf16-ragged-cols", seq_len=400, hidden=320, n_heads=5, n_kv_heads=5,
+        head_dim=64, ffn_dim=1344, q_block=200, kv_block=400, head_chunk=5),
+    "bf16-ragged-cols-swiglu": WORKLOADS["llama8b-s64k"].replace(
+        name="bf16-ragged-cols-swiglu", seq_len=400, hidden=320, n_heads=5, n_kv_heads=1,
+        head_dim=64, ffn_dim=1344, q_block=200, kv_block=400, head_chunk=5),
 }
 
 
